@@ -1,0 +1,88 @@
+"""Sigmoid router, biased top-k and unbiased gates -- test infrastructure.
+
+What is computed ([TP] section III: the affinity equation, the selection
+equation for g' and the normalisation equation for g; [VE] recipe step 4 and
+the glossary for u_t, e_i, b_i, K_r; [DF] "Balancing without a balance loss"):
+
+  s[t, i]  = sigmoid(u_t . e_i)                 each expert scored on its own
+  chosen   = the K_r experts with the largest s[t, i] + b[i]
+  g'[t, i] = s[t, i] if i is chosen else 0      (the bias never enters g')
+  g[t, i]  = g'[t, i] / sum_j g'[t, j]          (so the chosen gates sum to 1)
+
+Readings where the pages leave a step open:
+  * the router is x @ W_r^T with no router bias, temperature or extra scale;
+    here in float64 (bf16 x bf16 products are exact), sigmoid in float64;
+  * the scores that take part in selection and gating are float32, s32 =
+    fl32(s); the biased key is one float32 add, key = fl32(s32 + b);
+  * ties are broken by the lower expert index, and the k chosen experts are
+    listed in (key descending, index ascending) order;
+  * gates are computed in float64 from the float32 scores.
+"""
+import numpy as np
+
+
+def router_logits(x, w_r):
+    """z[t, i] = sum_h x[t, h] * W_r[i, h] in float64.  W_r row i is e_i."""
+    return np.asarray(x, np.float64) @ np.asarray(w_r, np.float64).T
+
+
+def sigmoid(z):
+    """1 / (1 + exp(-z)) in float64, evaluated without overflow."""
+    z = np.asarray(z, np.float64)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = ez / (1.0 + ez)
+    return out
+
+
+def router_scores(x, w_r):
+    """Float64 affinities s = sigmoid(x @ W_r^T)."""
+    return sigmoid(router_logits(x, w_r))
+
+
+def biased_keys(s32, bias):
+    """key = fl32(s32 + b), one float32 add per (token, expert)."""
+    s = np.asarray(s32, np.float32).astype(np.float64)
+    b = np.asarray(bias, np.float32).astype(np.float64)
+    return (s + b[None, :]).astype(np.float32)
+
+
+def select_topk(s32, bias, k):
+    """Indices [T, k] int32 of the k largest biased keys per token, ordered by
+    (key descending, index ascending)."""
+    key = biased_keys(s32, bias)
+    order = np.argsort(-key, axis=1, kind="stable")   # stable: index asc on ties
+    return order[:, :k].astype(np.int32)
+
+
+def gates(s32, idx):
+    """g[t, j] = s32[t, idx[t, j]] / sum_j' s32[t, idx[t, j']], float64.
+    The bias is not an argument: it cannot reach the gate."""
+    s = np.asarray(s32, np.float32).astype(np.float64)
+    sel = np.take_along_axis(s, np.asarray(idx, np.int64), axis=1)
+    tot = sel.sum(axis=1, keepdims=True)
+    k = sel.shape[1]
+    return np.where(tot > 0, sel / np.where(tot > 0, tot, 1.0), 1.0 / k)
+
+
+def route(x, w_r, bias, k):
+    """Full routing in the oracle's own precision.  Returns
+    (s64 [T,N] float64, s32 [T,N] float32, idx [T,k] int32, gate [T,k] float64)."""
+    s64 = router_scores(x, w_r)
+    s32 = s64.astype(np.float32)
+    idx = select_topk(s32, bias, k)
+    return s64, s32, idx, gates(s32, idx)
+
+
+def topk_margin(s64, bias, k):
+    """Float64 gap between the k-th and (k+1)-th largest s + b per token
+    (inf when k equals the number of experts).  A token with a tiny gap can be
+    routed either way by any finite-precision evaluation of the router."""
+    key = np.asarray(s64, np.float64) + np.asarray(bias, np.float64)[None, :]
+    n = key.shape[1]
+    if k >= n:
+        return np.full(key.shape[0], np.inf)
+    part = -np.sort(-key, axis=1)
+    return part[:, k - 1] - part[:, k]

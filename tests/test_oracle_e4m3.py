@@ -1,0 +1,122 @@
+"""Pins of the oracle's E4M3 codec against what the pages and the format fix.
+
+Sources: "DeepSeek-V3 Technical Report" (deepforge.srivtx.xyz), part 1
+"Per-tile FP8 scaling" (the E4M3 emulator: exponent clamped to [-6, 8], step
+2^(e-3), half-even rounding; 448 is the largest magnitude; eight steps per
+exponent) and part 4 "Build it yourself" (the 6-12 % per-element step).
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import e4m3
+
+
+def page_rule(x):
+    """The emulator the deepforge page describes, restated with exact
+    rationals: e = floor(log2|x|) clamped to [-6, 8], step 2^(e-3), the
+    quotient rounded half to even.  Unlike the kernel's reading it does not
+    saturate (it returns 480, 512, ... above 464)."""
+    if x == 0.0:
+        return 0.0
+    a = abs(x)
+    e = math.frexp(a)[1] - 1
+    e = max(-6, min(8, e))
+    step = Fraction(2) ** (e - 3)
+    q = round(Fraction(a) / step)          # Fraction rounding is half-even
+    return math.copysign(float(q * step), x)
+
+
+def test_table_shape():
+    pos = e4m3.POS_VALUES
+    assert pos.size == 127 and np.all(np.isfinite(pos))
+    assert np.all(np.diff(pos) > 0)                      # code order = value order
+    assert pos[-1] == 448.0 and pos[0] == 0.0
+    assert pos[1] == 2.0 ** -9                           # smallest subnormal
+    assert pos[8] == 2.0 ** -6                           # smallest normal
+    assert math.isnan(e4m3.TABLE[0x7F]) and math.isnan(e4m3.TABLE[0xFF])
+    assert np.array_equal(e4m3.TABLE[0x80:0xFF], -e4m3.TABLE[0x00:0x7F])
+
+
+def test_eight_steps_per_exponent():
+    pos = e4m3.POS_VALUES
+    for e in range(-6, 8):
+        n = np.sum((pos >= 2.0 ** e) & (pos < 2.0 ** (e + 1)))
+        assert n == 8, e
+    # the top binade stops at 448 = 1.75 * 2^8 (480 would be the NaN code)
+    assert np.sum(pos >= 256.0) == 7
+
+
+def test_relative_step_is_6_to_12_percent():
+    pos = e4m3.POS_VALUES
+    normal = pos[8:]
+    rel = np.diff(normal) / normal[:-1]
+    assert rel.min() >= 0.0625 - 1e-15 and rel.max() <= 0.125 + 1e-15
+
+
+def _fp32_sweep(stride=257):
+    bits = np.arange(0, 1 << 32, stride, dtype=np.uint64).astype(np.uint32)
+    v = bits.view(np.float32)
+    return v[np.isfinite(v)].astype(np.float64)
+
+
+def _ties_and_neighbours():
+    pos = e4m3.POS_VALUES
+    mids = np.concatenate([(pos[:-1] + pos[1:]) / 2, [464.0]])
+    out = [mids]
+    for direction in (np.inf, -np.inf):
+        cur = mids.astype(np.float32)
+        for _ in range(3):
+            cur = np.nextafter(cur, np.float32(direction))
+            out.append(cur.astype(np.float64))
+    vals = np.concatenate(out + [pos])
+    return np.concatenate([vals, -vals])
+
+
+def test_two_encoders_agree_on_a_float32_sweep():
+    v = _fp32_sweep()
+    assert np.array_equal(e4m3.encode_search(v), e4m3.encode_arith(v))
+
+
+def test_two_encoders_agree_on_ties():
+    v = _ties_and_neighbours()
+    assert np.array_equal(e4m3.encode_search(v), e4m3.encode_arith(v))
+
+
+def test_ties_go_to_even_code():
+    pos = e4m3.POS_VALUES
+    mids = (pos[:-1] + pos[1:]) / 2
+    codes = e4m3.encode(mids)
+    assert np.all(codes % 2 == 0)
+
+
+def test_matches_the_page_emulator_up_to_448():
+    rng = np.random.default_rng(1)
+    v = np.concatenate([
+        rng.uniform(-448, 448, 100000),
+        np.exp(rng.uniform(np.log(1e-4), np.log(448), 100000)) * rng.choice([-1, 1], 100000),
+        _ties_and_neighbours(),
+    ])
+    v = v[np.abs(v) <= 448.0].astype(np.float32).astype(np.float64)
+    want = np.array([page_rule(float(x)) for x in v])
+    got = e4m3.round_to_e4m3(v)
+    assert np.array_equal(got, want)
+
+
+def test_saturation_reading_differs_from_page_only_above_464():
+    # the page's emulator leaves the format above 464; the reading used here
+    # saturates every magnitude above 448 to 448
+    assert page_rule(470.0) == 480.0
+    assert e4m3.round_to_e4m3(470.0) == 448.0
+    assert page_rule(460.0) == 448.0 == e4m3.round_to_e4m3(460.0)
+    assert e4m3.encode(1e30) == 0x7E and e4m3.encode(-1e30) == 0xFE
+
+
+def test_sign_of_zero_is_kept():
+    assert e4m3.encode(0.0) == 0x00
+    assert e4m3.encode(-0.0) == 0x80
+    assert e4m3.encode(-1e-30) == 0x80
+    assert e4m3.encode(2.0 ** -11) == 0x00          # below half the smallest subnormal
+    assert e4m3.encode(2.0 ** -10 * 1.0000001) == 0x01

@@ -1,0 +1,143 @@
+"""Pins of the oracle's router, biased top-k and gates.
+
+Source: "DeepSeek-V3: Auxiliary-Loss-Free MoE Load Balancing, Multi-Token
+Prediction, and FP8 Training at 671B Scale", section III: the affinity
+equation s = Sigmoid(u . e), the selection equation (s + b in TopK), the gate
+normalisation g = g' / sum g' and the bullet "the bias only enters the TopK
+comparison"; "DeepSeek-V3, explained.", glossary (normalised weights sum to 1,
+bias decides which experts are chosen and never how much they count).
+"""
+import itertools
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+from oracle import route
+
+
+def _f32(v):
+    return np.asarray(v, np.float64).astype(np.float32)
+
+
+def test_sigmoid_closed_forms_and_library():
+    assert route.sigmoid(np.array([0.0]))[0] == 0.5
+    assert abs(route.sigmoid(np.array([np.log(3.0)]))[0] - 0.75) < 1e-15
+    z = np.linspace(-40, 40, 2001)
+    np.testing.assert_allclose(route.sigmoid(z) + route.sigmoid(-z), 1.0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(route.sigmoid(z), expit(z), rtol=1e-14, atol=0)
+    assert np.all(np.isfinite(route.sigmoid(np.array([-800.0, 800.0]))))
+
+
+def test_router_logits_closed_form():
+    T, H, N = 3, 256, 5
+    x = np.ones((T, H)) * np.array([1.0, 2.0, -0.5])[:, None]
+    w = np.arange(N)[:, None] / 256.0 * np.ones((N, H))
+    z = route.router_logits(x, w)
+    np.testing.assert_array_equal(z, np.array([1.0, 2.0, -0.5])[:, None] * np.arange(N)[None, :] * H / 256.0)
+    # one-hot tokens pick out columns of W_r: z[t, i] = W_r[i, t]
+    rng = np.random.default_rng(0)
+    w = rng.standard_normal((N, H))
+    np.testing.assert_array_equal(route.router_logits(np.eye(H)[:T], w), w[:, :T].T)
+
+
+def _brute_topk(key, k):
+    """The unique k-set S with: every member's key exceeds every non-member's,
+    ties resolved to the lower index; listed by (key desc, index asc)."""
+    n = key.size
+    found = []
+    for S in itertools.combinations(range(n), k):
+        rest = [j for j in range(n) if j not in S]
+        ok = all(key[i] > key[j] or (key[i] == key[j] and i < j) for i in S for j in rest)
+        if ok:
+            found.append(S)
+    assert len(found) == 1
+    S = list(found[0])
+    S.sort(key=lambda i: (-key[i], i))
+    return S
+
+
+@pytest.mark.parametrize("n,k", [(6, 2), (8, 3), (7, 7), (9, 1)])
+def test_topk_matches_brute_force(n, k):
+    rng = np.random.default_rng(n * 10 + k)
+    for trial in range(40):
+        s = _f32(rng.uniform(0, 1, (1, n)))
+        b = _f32(rng.uniform(-0.1, 0.1, n))
+        if trial % 3 == 0:                                  # force ties
+            s = _f32(np.round(s * 4) / 4)
+            b = np.zeros(n, np.float32)
+        idx = route.select_topk(s, b, k)[0]
+        key = route.biased_keys(s, b)[0]
+        assert list(idx) == _brute_topk(key, k)
+
+
+def test_k_equals_n_is_plain_normalisation():
+    rng = np.random.default_rng(7)
+    s = _f32(rng.uniform(0.01, 1, (5, 6)))
+    b = _f32(rng.uniform(-1, 1, 6))
+    idx = route.select_topk(s, b, 6)
+    assert all(sorted(r) == list(range(6)) for r in idx)
+    g = route.gates(s, idx)
+    full = s.astype(np.float64) / s.astype(np.float64).sum(1, keepdims=True)
+    np.testing.assert_allclose(np.take_along_axis(full, idx.astype(np.int64), 1), g, rtol=1e-15)
+
+
+def test_zero_bias_is_textbook_topk_of_sigmoid():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((50, 128))
+    w = rng.standard_normal((16, 128)) * 0.1
+    s64, s32, idx, g = route.route(x, w, np.zeros(16, np.float32), 4)
+    ref = np.argsort(-s32.astype(np.float64), axis=1, kind="stable")[:, :4]
+    assert np.array_equal(idx, ref)
+
+
+def test_large_bias_forces_selection_but_not_the_gate():
+    rng = np.random.default_rng(9)
+    s = _f32(rng.uniform(0, 1, (100, 16)))
+    b = np.zeros(16, np.float32)
+    b[3] = 10.0
+    idx = route.select_topk(s, b, 2)
+    assert np.all(idx[:, 0] == 3)
+    g = route.gates(s, idx)
+    want = s[:, 3].astype(np.float64) / (s[:, 3].astype(np.float64)
+                                         + np.take_along_axis(s, idx[:, 1:2].astype(np.int64), 1)[:, 0])
+    np.testing.assert_array_equal(g[:, 0], want)
+
+
+def test_gates_are_invariant_to_bias_that_keeps_the_selection():
+    rng = np.random.default_rng(10)
+    s = _f32(rng.uniform(0, 1, (200, 16)))
+    b1 = _f32(rng.uniform(-0.05, 0.05, 16))
+    b2 = _f32(b1 + rng.uniform(-1e-3, 1e-3, 16))
+    i1, i2 = route.select_topk(s, b1, 4), route.select_topk(s, b2, 4)
+    same = np.all(np.sort(i1, 1) == np.sort(i2, 1), axis=1)
+    assert same.sum() > 150
+    g1 = route.gates(s, np.sort(i1, 1))
+    g2 = route.gates(s, np.sort(i2, 1))
+    assert np.array_equal(g1[same], g2[same])
+
+
+def test_gates_sum_to_one_and_are_positive():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((300, 64))
+    w = rng.standard_normal((32, 64)) * 0.2
+    _, s32, idx, g = route.route(x, w, _f32(rng.uniform(-0.1, 0.1, 32)), 8)
+    assert np.all(g > 0)
+    np.testing.assert_allclose(g.sum(1), 1.0, rtol=0, atol=1e-15)
+    assert np.all(np.diff(route.biased_keys(s32, _f32(np.zeros(32)))[0]) != np.inf)
+
+
+def test_order_is_key_descending():
+    rng = np.random.default_rng(12)
+    s = _f32(rng.uniform(0, 1, (100, 32)))
+    b = _f32(rng.uniform(-0.05, 0.05, 32))
+    idx = route.select_topk(s, b, 8)
+    key = np.take_along_axis(route.biased_keys(s, b), idx.astype(np.int64), 1)
+    assert np.all(np.diff(key.astype(np.float64), axis=1) <= 0)
+
+
+def test_margin():
+    s = np.array([[0.9, 0.5, 0.4, 0.1]])
+    b = np.array([0.0, 0.0, 0.05, 0.0])
+    assert abs(route.topk_margin(s, b, 2)[0] - (0.5 - 0.45)) < 1e-15
+    assert route.topk_margin(s, b, 4)[0] == np.inf
