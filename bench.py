@@ -1,0 +1,217 @@
+"""Benchmark of the DeepSeekMoE forward layer (FP8 block-scaled, sigmoid router)
+on one MI355X.
+
+A step is one forward pass of the whole layer over one batch: router + biased
+top-k, permutation, 1x128 activation quantisation, grouped FP8 GEMM 1 with the
+SwiGLU + re-quantisation epilogue, grouped FP8 GEMM 2, combine, bias update.
+Weights are quantised 128x128 once before timing (a per-weight-update cost,
+reported separately).  Inputs are seeded synthetic tensors generated on the
+device, resident in HBM before the timed region.
+
+Prints ONE JSON line.  Default workload: the DeepSeek-V3-shaped layer at
+prefill size (T = 8192, H 7168, 256 routed experts top-8 + 1 shared, I 2048).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill",
+                    choices=["prefill", "decode", "skew", "routing", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, sample_tokens=1024):
+    """The oracle, untuned, on a bounded sample of the same workload.
+
+    Sample: the first `sample_tokens` tokens of the batch.  Routing, the
+    activation quantisation, the permutation, the combine and the bias update
+    run on the whole sample; the expert FFN runs on every sample row of the
+    shared expert and of the two routed experts with the most sample rows, and
+    its per-row time is scaled to the sample's T*(k+1) rows (the per-row cost
+    of the FFN does not depend on which expert the row belongs to).  Result:
+    tokens per second of the whole layer on the host."""
+    import synth
+    from oracle import bias as obias, ffn, permute as operm, quant, route
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    S = min(sample_tokens, w.T)
+    x = synth.as_f64(synth.generate(w.x_spec(), w.seed, rows=np.arange(S)))
+    wr = synth.as_f64(w.router_weight())
+    b = w.bias()
+    t0 = time.perf_counter()
+    s64, s32, idx, gate = route.route(x, wr, b, w.k)
+    xq, xd = quant.quant_1x128(x)
+    counts, offsets, row_of, token_of = operm.permute(idx, w.N, True)
+    t_route = time.perf_counter() - t0
+    top = np.argsort(-counts, kind="stable")[:2]
+    experts = [w.N] + [int(e) for e in top]
+    rows_done, t_ffn = 0, 0.0
+    out = np.zeros((S * w.k + S, w.H))
+    for g in experts:
+        H, I = w.H, w.I
+        w1 = synth.as_f64(synth.generate(w.w1_spec(), w.seed, rows=np.arange(g * 2 * I, (g + 1) * 2 * I)))
+        w2 = synth.as_f64(synth.generate(w.w2_spec(), w.seed, rows=np.arange(g * H, (g + 1) * H)))
+        w1q, w1d = quant.quant_128x128(w1)
+        w2q, w2d = quant.quant_128x128(w2)
+        del w1, w2
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        toks = token_of[r0:r1]
+        t1 = time.perf_counter()
+        res = ffn.expert_ffn(xq[toks], xd[toks], w1q, w1d, w2q, w2d, "D")
+        t_ffn += time.perf_counter() - t1
+        out[r0:r1] = res["out"]
+        rows_done += r1 - r0
+    t2 = time.perf_counter()
+    ffn.combine(out, gate, row_of, S * w.k, "D")
+    obias.bias_update(b, counts, S, w.k, w.gamma)
+    t_tail = time.perf_counter() - t2
+    t_total = t_route + t_tail + t_ffn / rows_done * (S * (w.k + 1))
+    return {"value": S / t_total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"{S} tokens of the {w.name} batch: routing, quantisation, permutation, "
+                       f"combine and bias update on all {S}; expert FFN timed on {rows_done} rows "
+                       f"(shared expert + 2 most-loaded routed experts) and scaled per row to "
+                       f"{S * (w.k + 1)} rows"),
+            "measured_s": round(t_route + t_ffn + t_tail, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the expert-parallel design across GPUs is described, not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import fp8_block_scaled_sigmoid_amd as moe
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+
+    def gen(spec, seed=w.seed):
+        t = torch.empty(spec.shape, dtype=torch.bfloat16, device=dev)
+        synth.device_generate(spec, seed, t)
+        return t
+
+    wr = torch.from_numpy(w.router_weight().view(np.int16)).view(torch.bfloat16).to(dev)
+    bias = torch.from_numpy(w.bias().copy()).to(dev)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w1 = gen(w.w1_spec())
+    e0.record(st)
+    w1q, w1d = moe.fp8_quant_128x128(w1, interleave_gate_up=True)
+    e1.record(st)
+    torch.cuda.synchronize()
+    t_wq1 = e0.elapsed_time(e1)
+    del w1
+    w2 = gen(w.w2_spec())
+    e0.record(st)
+    w2q, w2d = moe.fp8_quant_128x128(w2)
+    e1.record(st)
+    torch.cuda.synchronize()
+    t_wq2 = e0.elapsed_time(e1)
+    del w2
+    torch.cuda.empty_cache()
+    weights = moe.MoEWeights(wr, bias, w1q=w1q, w1d=w1d, w2q=w2q, w2d=w2d)
+    lay = moe.MoELayer(weights, w.T, w.k, w.gamma, device=dev)
+    x = gen(w.x_spec())
+
+    names = ["route", "permute", "quant_x", "gemm1", "gemm2", "combine", "bias"]
+    fns = [lambda: lay.route(x), lay.permute, lambda: lay.quant_x(x), lay.gemm1, lay.gemm2,
+           lay.combine, lay.bias_update]
+
+    def step(evs=None):
+        for i, f in enumerate(fns):
+            if evs is not None:
+                evs[i][0].record(st)
+            f()
+            if evs is not None:
+                evs[i][1].record(st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # whole-step timing (no per-kernel events inside)
+    t0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(args.steps):
+        step()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+    # per-kernel timing: the same steps again with events around each launch
+    per = {n: [] for n in names}
+    for _ in range(args.steps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in names]
+        step(evs)
+        torch.cuda.synchronize()
+        for n, (a, b) in zip(names, evs):
+            per[n].append(a.elapsed_time(b))
+    kern = {n: float(np.mean(v)) for n, v in per.items()}
+
+    R = w.R
+    g1_flops = 2.0 * R * w.H * 2 * w.I
+    g2_flops = 2.0 * R * w.I * w.H
+    gemm_tflops = (g1_flops + g2_flops) / ((kern["gemm1"] + kern["gemm2"]) * 1e-3) / 1e12
+    g1_tflops = g1_flops / (kern["gemm1"] * 1e-3) / 1e12
+    tokens_per_s = w.T / (ms_step * 1e-3)
+
+    res = {
+        "metric": "MoE layer tokens/s (DeepSeek-V3 shape, FP8 block-scaled, 1 GPU)",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded counter-based generator, generated on the device)",
+        "config": {"workload": f"{w.name}: T={w.T} tokens, hidden {w.H}, {w.N} routed experts "
+                               f"top-{w.k} + 1 shared, SwiGLU intermediate {w.I}, FP8 E4M3 "
+                               f"1x128 / 128x128 scales",
+                   "T": w.T, "H": w.H, "N": w.N, "k": w.k, "I": w.I},
+        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_kernel<SWIGLU_FP8> (GEMM1)",
+                     "achieved": round(g1_tflops, 2), "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(g1_tflops / FP8_PEAK_TFLOPS, 4),
+                     "traffic": None,
+                     "algorithmic_flops_per_launch": g1_flops},
+        "gemm_tflops": round(gemm_tflops, 2),
+        "gemm_frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
+        "kernel_ms": {n: round(v, 4) for n, v in kern.items()},
+        "weight_quant_ms": round(t_wq1 + t_wq2, 3),
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline and w.with_experts:
+        res["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,322 @@
+"""Python binding of libmoe_fp8.so: the DeepSeekMoE forward layer on MI355X.
+
+Argument marshalling only.  Every step of the layer runs in the HIP kernels
+behind the C ABI declared in ``include/moe_fp8.h``; PyTorch is used for device
+memory and the current stream, nothing else.  There is no fallback: if the
+library is missing or the device is not gfx950 the calls raise.
+
+The functions carry the C entry points' names.  ``MoELayer`` chains them into
+the forward pass (router + biased top-k, permutation, 1x128 activation
+quantisation, the two grouped FP8 GEMMs, combine, bias update).
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_fp8.so")
+
+MOE_BF16, MOE_F32 = 0, 1
+MOE_EPI_BF16, MOE_EPI_SWIGLU_FP8, MOE_EPI_F32 = 0, 1, 2
+
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",
+          4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_DEVICE", 6: "MOE_ERR_UNSUPPORTED",
+          7: "MOE_ERR_HIP"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, code, hip=0):
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)}"
+                         + (f" (hipError {hip})" if code == 7 else ""))
+        self.code = code
+
+
+class GemmArgs(ctypes.Structure):
+    _fields_ = [("a_q", ctypes.c_void_p), ("a_d", ctypes.c_void_p), ("lda", ctypes.c_int),
+                ("a_rows", ctypes.c_int), ("a_row_index", ctypes.c_void_p),
+                ("b_q", ctypes.c_void_p), ("b_d", ctypes.c_void_p),
+                ("group_offsets", ctypes.c_void_p), ("num_groups", ctypes.c_int),
+                ("total_rows", ctypes.c_int), ("n_out", ctypes.c_int), ("k_dim", ctypes.c_int),
+                ("epilogue", ctypes.c_int), ("out", ctypes.c_void_p), ("out_d", ctypes.c_void_p),
+                ("ldo", ctypes.c_int), ("row_scale", ctypes.c_void_p)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+
+
+def lib():
+    """Load libmoe_fp8.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "moe_route_topk": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P],
+            "moe_topk_from_scores": [_P, _P, _I, _I, _I, _P, _P, _P],
+            "moe_permute": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+            "fp8_quant_1x128": [_P, _I, _I, _I, _I, _P, _P, _P],
+            "fp8_quant_128x128": [_P, _I, _I, _I, _I, _P, _P, _P],
+            "moe_grouped_gemm_fp8": [ctypes.POINTER(GemmArgs), _P],
+            "moe_combine": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P],
+            "moe_bias_update": [_P, _P, _I, _I, _I, ctypes.c_float, _P],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.moe_permute_workspace_bytes.argtypes = [_I, _I, _I]
+        L.moe_permute_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_status_str.argtypes = [_I]
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_last_hip_error.argtypes = []
+        L.moe_last_hip_error.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(name, rc):
+    if rc != 0:
+        raise MoeError(name, rc, lib().moe_last_hip_error() if rc == 7 else 0)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if not (t.is_cuda and t.dtype == dtype and t.is_contiguous()):
+        raise ValueError(f"{name}: need a contiguous {dtype} device tensor, got "
+                         f"{t.dtype} on {t.device} (contiguous={t.is_contiguous()})")
+    return t
+
+
+# ---------------------------------------------------------------------------
+# the C entry points
+
+
+def moe_route_topk(x, w_router, bias, k, scores=True, idx=None, gate=None, stream=None):
+    """Sigmoid router + biased top-k.  x [T,H] bf16, w_router [N,H] bf16,
+    bias [N] float32.  Returns (idx int32 [T,k], gate float32 [T,k],
+    scores float32 [T,N] or None)."""
+    T, H = x.shape
+    N = w_router.shape[0]
+    _dev(x, torch.bfloat16, "x"), _dev(w_router, torch.bfloat16, "w_router")
+    _dev(bias, torch.float32, "bias")
+    if scores is True:
+        scores = torch.empty(T, N, dtype=torch.float32, device=x.device)
+    elif scores is False:
+        scores = None
+    idx = torch.empty(T, k, dtype=torch.int32, device=x.device) if idx is None else idx
+    gate = torch.empty(T, k, dtype=torch.float32, device=x.device) if gate is None else gate
+    _check("moe_route_topk", lib().moe_route_topk(_ptr(x), _ptr(w_router), _ptr(bias), T, H, N, k,
+                                                  _ptr(scores), _ptr(idx), _ptr(gate),
+                                                  _stream(stream)))
+    return idx, gate, scores
+
+
+def moe_topk_from_scores(scores, bias, k, idx=None, gate=None, stream=None):
+    T, N = scores.shape
+    _dev(scores, torch.float32, "scores"), _dev(bias, torch.float32, "bias")
+    idx = torch.empty(T, k, dtype=torch.int32, device=scores.device) if idx is None else idx
+    gate = torch.empty(T, k, dtype=torch.float32, device=scores.device) if gate is None else gate
+    _check("moe_topk_from_scores", lib().moe_topk_from_scores(
+        _ptr(scores), _ptr(bias), T, N, k, _ptr(idx), _ptr(gate), _stream(stream)))
+    return idx, gate
+
+
+def moe_permute_workspace_bytes(T, N, k):
+    return int(lib().moe_permute_workspace_bytes(T, N, k))
+
+
+def moe_permute(idx, N, with_shared=True, out=None, ws=None, stream=None):
+    """idx int32 [T,k] -> (counts [N], offsets [N+2], row_of [T,k],
+    token_of [T*k (+T)]), all int32."""
+    T, k = idx.shape
+    _dev(idx, torch.int32, "idx")
+    dev = idx.device
+    if out is None:
+        R = T * k + (T if with_shared else 0)
+        out = (torch.empty(N, dtype=torch.int32, device=dev),
+               torch.empty(N + 2, dtype=torch.int32, device=dev),
+               torch.empty(T, k, dtype=torch.int32, device=dev),
+               torch.empty(R, dtype=torch.int32, device=dev))
+    counts, offsets, row_of, token_of = out
+    nbytes = moe_permute_workspace_bytes(T, N, k)
+    if ws is None:
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    _check("moe_permute", lib().moe_permute(_ptr(idx), T, N, k, 1 if with_shared else 0,
+                                            _ptr(counts), _ptr(offsets), _ptr(row_of),
+                                            _ptr(token_of), _ptr(ws), ws.numel(),
+                                            _stream(stream)))
+    return counts, offsets, row_of, token_of
+
+
+def fp8_quant_1x128(x, q=None, d=None, stream=None):
+    """x [rows, cols] bf16 or float32 -> (q uint8 [rows, cols], d float32 [rows, cols/128])."""
+    rows, cols = x.shape
+    dt = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}[x.dtype]
+    if x.stride(1) != 1:
+        raise ValueError("x: rows must be contiguous")
+    q = torch.empty(rows, cols, dtype=torch.uint8, device=x.device) if q is None else q
+    d = torch.empty(rows, cols // 128, dtype=torch.float32, device=x.device) if d is None else d
+    _check("fp8_quant_1x128", lib().fp8_quant_1x128(_ptr(x), dt, rows, cols, x.stride(0), _ptr(q),
+                                                    _ptr(d), _stream(stream)))
+    return q, d
+
+
+def fp8_quant_128x128(w, interleave_gate_up=False, q=None, d=None, stream=None):
+    """w [batch, rows, cols] bf16 -> (q uint8 like w, d float32 [batch, rows/128, cols/128])."""
+    if w.dim() == 2:
+        w = w.unsqueeze(0)
+    B, rows, cols = w.shape
+    _dev(w, torch.bfloat16, "w")
+    q = torch.empty(B, rows, cols, dtype=torch.uint8, device=w.device) if q is None else q
+    d = torch.empty(B, rows // 128, cols // 128, dtype=torch.float32, device=w.device) \
+        if d is None else d
+    _check("fp8_quant_128x128", lib().fp8_quant_128x128(_ptr(w), B, rows, cols,
+                                                        1 if interleave_gate_up else 0, _ptr(q),
+                                                        _ptr(d), _stream(stream)))
+    return q, d
+
+
+def moe_grouped_gemm_fp8(a_q, a_d, b_q, b_d, group_offsets, total_rows, epilogue,
+                         a_row_index=None, out=None, out_d=None, row_scale=None, stream=None):
+    """Grouped block-scaled FP8 GEMM (see include/moe_fp8.h).  b_q [G, n_out, K]."""
+    G, n_out, K = b_q.shape
+    dev = a_q.device
+    if out is None:
+        if epilogue == MOE_EPI_SWIGLU_FP8:
+            out = torch.empty(total_rows, n_out // 2, dtype=torch.uint8, device=dev)
+            out_d = torch.empty(total_rows, n_out // 256, dtype=torch.float32, device=dev)
+        elif epilogue == MOE_EPI_BF16:
+            out = torch.empty(total_rows, n_out, dtype=torch.bfloat16, device=dev)
+        else:
+            out = torch.empty(total_rows, n_out, dtype=torch.float32, device=dev)
+    args = GemmArgs(a_q.data_ptr(), a_d.data_ptr(), a_q.stride(0), a_q.shape[0],
+                    a_row_index.data_ptr() if a_row_index is not None else None,
+                    b_q.data_ptr(), b_d.data_ptr(), group_offsets.data_ptr(), G, total_rows,
+                    n_out, K, epilogue, out.data_ptr(),
+                    out_d.data_ptr() if out_d is not None else None, out.stride(0),
+                    row_scale.data_ptr() if row_scale is not None else None)
+    _check("moe_grouped_gemm_fp8", lib().moe_grouped_gemm_fp8(ctypes.byref(args), _stream(stream)))
+    return out, out_d
+
+
+def moe_combine(out_rows, gate, row_of, shared_row0, residual=None, y=None, stream=None):
+    T, k = row_of.shape
+    H = out_rows.shape[1]
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=out_rows.device) if y is None else y
+    _check("moe_combine", lib().moe_combine(_ptr(out_rows), _ptr(gate), _ptr(row_of), shared_row0,
+                                            T, H, k, _ptr(residual), _ptr(y), _stream(stream)))
+    return y
+
+
+def moe_bias_update(bias, counts, T, k, gamma, stream=None):
+    N = bias.shape[0]
+    _check("moe_bias_update", lib().moe_bias_update(_ptr(bias), _ptr(counts), N, T, k,
+                                                    float(gamma), _stream(stream)))
+    return bias
+
+
+# ---------------------------------------------------------------------------
+# the layer
+
+
+class MoEWeights:
+    """Device weights of one layer: router [N,H] bf16, bias [N] float32, and
+    FP8 experts quantised 128x128 from bf16 W1 [G,2I,H] (gate rows, then up
+    rows) and W2 [G,H,I]; expert G-1 = N is the shared expert."""
+
+    def __init__(self, w_router, bias, w1_bf16=None, w2_bf16=None, w1q=None, w1d=None,
+                 w2q=None, w2d=None):
+        self.w_router = w_router
+        self.bias = bias
+        if w1_bf16 is not None:
+            w1q, w1d = fp8_quant_128x128(w1_bf16, interleave_gate_up=True)
+        if w2_bf16 is not None:
+            w2q, w2d = fp8_quant_128x128(w2_bf16)
+        self.w1q, self.w1d, self.w2q, self.w2d = w1q, w1d, w2q, w2d
+        self.N, self.H = w_router.shape
+        self.G = w1q.shape[0]
+        self.I = w1q.shape[1] // 2
+
+
+class MoELayer:
+    """Buffers for a batch of T tokens and the forward pass over them.  All
+    buffers are allocated once here; ``forward`` only enqueues kernels."""
+
+    def __init__(self, weights, T, k, gamma=1e-3, device="cuda"):
+        w = weights
+        self.w, self.T, self.k, self.gamma = w, T, k, gamma
+        N, H, I = w.N, w.H, w.I
+        self.with_shared = w.G == N + 1
+        R = T * k + (T if self.with_shared else 0)
+        self.R = R
+        e = dict(device=device)
+        self.scores = torch.empty(T, N, dtype=torch.float32, **e)
+        self.idx = torch.empty(T, k, dtype=torch.int32, **e)
+        self.gate = torch.empty(T, k, dtype=torch.float32, **e)
+        self.counts = torch.empty(N, dtype=torch.int32, **e)
+        self.offsets = torch.empty(N + 2, dtype=torch.int32, **e)
+        self.row_of = torch.empty(T, k, dtype=torch.int32, **e)
+        self.token_of = torch.empty(R, dtype=torch.int32, **e)
+        self.ws = torch.empty(max(moe_permute_workspace_bytes(T, N, k), 16), dtype=torch.uint8, **e)
+        self.xq = torch.empty(T, H, dtype=torch.uint8, **e)
+        self.xd = torch.empty(T, H // 128, dtype=torch.float32, **e)
+        self.hq = torch.empty(R, I, dtype=torch.uint8, **e)
+        self.hd = torch.empty(R, I // 128, dtype=torch.float32, **e)
+        self.out_rows = torch.empty(R, H, dtype=torch.bfloat16, **e)
+        self.y = torch.empty(T, H, dtype=torch.bfloat16, **e)
+
+    # the individual steps, so that callers can time or replace one of them
+    def route(self, x, stream=None):
+        moe_route_topk(x, self.w.w_router, self.w.bias, self.k, scores=self.scores, idx=self.idx,
+                       gate=self.gate, stream=stream)
+
+    def permute(self, stream=None):
+        moe_permute(self.idx, self.w.N, self.with_shared,
+                    out=(self.counts, self.offsets, self.row_of, self.token_of), ws=self.ws,
+                    stream=stream)
+
+    def quant_x(self, x, stream=None):
+        fp8_quant_1x128(x, q=self.xq, d=self.xd, stream=stream)
+
+    def gemm1(self, stream=None):
+        moe_grouped_gemm_fp8(self.xq, self.xd, self.w.w1q, self.w.w1d, self.offsets, self.R,
+                             MOE_EPI_SWIGLU_FP8,
+                             a_row_index=self.token_of, out=self.hq, out_d=self.hd, stream=stream)
+
+    def gemm2(self, stream=None):
+        moe_grouped_gemm_fp8(self.hq, self.hd, self.w.w2q, self.w.w2d, self.offsets, self.R,
+                             MOE_EPI_BF16, out=self.out_rows, stream=stream)
+
+    def combine(self, stream=None):
+        moe_combine(self.out_rows, self.gate, self.row_of,
+                    self.T * self.k if self.with_shared else -1, y=self.y, stream=stream)
+
+    def bias_update(self, stream=None):
+        moe_bias_update(self.w.bias, self.counts, self.T, self.k, self.gamma, stream=stream)
+
+    def forward(self, x, update_bias=True, stream=None):
+        """One forward pass of the layer over x [T,H] bf16; returns y [T,H]
+        bf16 (a buffer of this object).  With update_bias the per-expert bias
+        is updated from this batch's counts at the end."""
+        self.route(x, stream)
+        self.permute(stream)
+        self.quant_x(x, stream)
+        self.gemm1(stream)
+        self.gemm2(stream)
+        self.combine(stream)
+        if update_bias:
+            self.bias_update(stream)
+        return self.y

@@ -1,0 +1,124 @@
+// Gate-weighted combine and the sign-based bias update.
+//
+// Combine ("DeepSeek-V3, explained.", glossary: routed weights sum to 1, the
+// shared expert is added at full weight; "DeepSeek-V3: Auxiliary-Loss-Free MoE
+// Load Balancing, ...", Figure 2: expert outputs are summed into the block
+// output).  An HBM stream: each lane owns 8 columns of one token, issues the
+// k + 1 independent 16-byte row loads together, and accumulates in float with
+// one fused multiply-add per slot in slot order, so the result does not depend
+// on the launch shape.
+//
+// Bias update (same page, section III "How the bias is set"; "DeepSeek-V3,
+// explained.", recipe step 4): overloaded experts lose gamma, underloaded ones
+// gain gamma, judged by an exact integer comparison of N * count with T * k.
+#include "common.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr int kCombineBlock = 256;
+
+__global__ __launch_bounds__(kCombineBlock) void combine_kernel(
+    const uint16_t* __restrict__ out, const float* __restrict__ gate,
+    const int32_t* __restrict__ row_of, int shared_row0, int T, int H, int k,
+    const uint16_t* __restrict__ residual, uint16_t* __restrict__ y) {
+  const int c8 = blockIdx.x * kCombineBlock + threadIdx.x;  // 8-column chunk
+  if (c8 * 8 >= H) return;
+  for (int t = blockIdx.y; t < T; t += gridDim.y) {
+    float acc[8];
+    const long long col = (long long)c8 * 8;
+    uint4 base = make_uint4(0, 0, 0, 0);
+    if (shared_row0 >= 0)
+      base = *reinterpret_cast<const uint4*>(out + (long long)(shared_row0 + t) * H + col);
+    const uint32_t bw[4] = {base.x, base.y, base.z, base.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = bf16_lo(bw[i]);
+      acc[2 * i + 1] = bf16_hi(bw[i]);
+    }
+    if (residual) {
+      const uint4 r = *reinterpret_cast<const uint4*>(residual + (long long)t * H + col);
+      const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = bf16_lo(rw[i]) + acc[2 * i];
+        acc[2 * i + 1] = bf16_hi(rw[i]) + acc[2 * i + 1];
+      }
+    }
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      const int jn = min(8, k - j0);
+      uint4 rows[8];
+      float g[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < jn) {
+          const int r = row_of[(long long)t * k + j0 + j];
+          g[j] = gate[(long long)t * k + j0 + j];
+          rows[j] = *reinterpret_cast<const uint4*>(out + (long long)r * H + col);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < jn) {
+          const uint32_t w[4] = {rows[j].x, rows[j].y, rows[j].z, rows[j].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = __builtin_fmaf(g[j], bf16_lo(w[i]), acc[2 * i]);
+            acc[2 * i + 1] = __builtin_fmaf(g[j], bf16_hi(w[i]), acc[2 * i + 1]);
+          }
+        }
+      }
+    }
+    uint4 o;
+    o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+    o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+    o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
+    o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+    *reinterpret_cast<uint4*>(y + (long long)t * H + col) = o;
+  }
+}
+
+__global__ __launch_bounds__(256) void bias_update_kernel(float* __restrict__ bias,
+                                                           const int32_t* __restrict__ counts,
+                                                           int N, long long target, float gamma) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < N; i += gridDim.x * 256) {
+    const long long load = (long long)N * counts[i];
+    float step = 0.0f;
+    if (load > target) step = -gamma;
+    if (load < target) step = gamma;
+    bias[i] = bias[i] + step;
+  }
+}
+
+}  // namespace
+
+extern "C" moe_status_t moe_combine(const void* out_rows_bf16, const float* gate,
+                                    const int32_t* row_of, int shared_row0, int T, int H, int k,
+                                    const void* residual_bf16, void* y_bf16, hipStream_t stream) {
+  if (T < 0 || H < 0 || k < 0 || H % 8 != 0) return MOE_ERR_SHAPE;
+  if (T == 0 || H == 0) return MOE_OK;
+  if (!out_rows_bf16 || !y_bf16 || (k > 0 && (!gate || !row_of))) return MOE_ERR_NULL;
+  if (!aligned16(out_rows_bf16) || !aligned16(y_bf16) ||
+      (residual_bf16 && !aligned16(residual_bf16)))
+    return MOE_ERR_ALIGN;
+  if (moe_status_t s = check_device()) return s;
+  const int cblocks = (H / 8 + kCombineBlock - 1) / kCombineBlock;
+  const int ty = T < 65535 ? T : 65535;
+  hipLaunchKernelGGL(combine_kernel, dim3(cblocks, ty), dim3(kCombineBlock), 0, stream,
+                     static_cast<const uint16_t*>(out_rows_bf16), gate, row_of, shared_row0, T, H,
+                     k, static_cast<const uint16_t*>(residual_bf16), static_cast<uint16_t*>(y_bf16));
+  return launch_status();
+}
+
+extern "C" moe_status_t moe_bias_update(float* bias, const int32_t* counts, int N, int T, int k,
+                                        float gamma, hipStream_t stream) {
+  if (N < 0 || T < 0 || k < 0) return MOE_ERR_SHAPE;
+  if (N == 0) return MOE_OK;
+  if (!bias || !counts) return MOE_ERR_NULL;
+  if (moe_status_t s = check_device()) return s;
+  const int blocks = (N + 255) / 256;
+  hipLaunchKernelGGL(bias_update_kernel, dim3(blocks), dim3(256), 0, stream, bias, counts, N,
+                     (long long)T * k, gamma);
+  return launch_status();
+}

@@ -1,0 +1,83 @@
+// Shared device and host helpers of libmoe_fp8.so (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_fp8.h"
+
+#ifndef __HIP_DEVICE_COMPILE__
+#include <cstring>
+#endif
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// E4M3 ("fn", max 448) encoder: round to nearest, ties to the even code,
+// saturating, sign kept.  Written from the format's definition: three mantissa
+// bits on a grid of step 2^(e-3) for normal magnitudes 2^-6 <= |v| < 448, and
+// a fixed step of 2^-9 below 2^-6.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x43E00000u) {            // |v| >= 448: saturate
+    code = 0x7Eu;
+  } else if (a < 0x3C800000u) {      // |v| < 2^-6: multiples of 2^-9 (0..8)
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  } else {                           // keep 3 of the 23 mantissa bits, RNE
+    const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+    code = r - (120u << 3);          // exponent bias 127 -> 7
+  }
+  return code | sign;
+}
+
+// float -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Quantisation multiplier and stored factor of a tile with absolute maximum
+// amax: m = fl32(448 / amax), d = fl32(amax / 448); a zero tile, or one whose m
+// overflows, gets m = 0 (all codes 0x00) and d = 1.
+__device__ __forceinline__ void tile_scale(float amax, float& m, float& d) {
+  m = 448.0f / amax;
+  d = amax / 448.0f;
+  if (!(amax > 0.0f) || !(m <= 3.402823466e38f)) {
+    m = 0.0f;
+    d = 1.0f;
+  }
+}
+
+// Code of x * m with the zero-tile rule (m == 0 gives +0 -> 0x00).
+__device__ __forceinline__ uint32_t quant_code(float x, float m) {
+  return m == 0.0f ? 0u : e4m3_encode(x * m);
+}
+
+template <int WIDTH>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ int ceil_div_dev(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace moe
+
+// ---------------------------------------------------------------------------
+// host side
+namespace moe {
+
+moe_status_t check_device();                  // MOE_ERR_DEVICE unless gfx950
+moe_status_t hip_fail(hipError_t e);          // records e, returns MOE_ERR_HIP
+moe_status_t launch_status();                 // hipGetLastError -> status
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace moe

@@ -1,0 +1,149 @@
+// Per-expert counts and the token permutation: every (token, slot) assignment
+// gets its own row, nothing is dropped ("DeepSeek-V3, explained.", recipe
+// step 5), and the counts are the per-expert load the bias controller reads
+// ("DeepSeek-V3: Auxiliary-Loss-Free MoE Load Balancing, ...", section III
+// flowchart).
+//
+// A deterministic counting sort in three small launches, with no atomic
+// deciding any order:
+//   1. per block of 256 tokens: an LDS bit matrix mask[expert][token] (atomic
+//      OR only sets bits, so it is order-free); the block's count per expert is
+//      a popcount of its row, and an assignment's rank inside the block is the
+//      popcount of the bits of earlier tokens;
+//   2. one block scans the block counts per expert (block-major), then the
+//      expert totals, giving counts, offsets and each block's base row;
+//   3. row = offsets[e] + block base + in-block rank; token_of[row] = t, and the
+//      shared group's rows T*k + t -> t.
+// Rows of one group therefore come in token order.  The k experts of a token
+// must be distinct (as top-k makes them); otherwise rows are unspecified but
+// stay in bounds.
+#include "common.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr int kTokPerBlock = 256;
+constexpr int kWords = kTokPerBlock / 32;
+constexpr int kMaxExperts = 1024;
+
+__global__ __launch_bounds__(256) void permute_count_kernel(const int32_t* __restrict__ idx,
+                                                             int T, int N, int k,
+                                                             int32_t* __restrict__ blk_counts,
+                                                             int32_t* __restrict__ rank) {
+  __shared__ uint32_t mask[kMaxExperts * kWords];
+  const int b = blockIdx.x;
+  const int t0 = b * kTokPerBlock;
+  for (int i = threadIdx.x; i < N * kWords; i += 256) mask[i] = 0u;
+  __syncthreads();
+  const int t = t0 + threadIdx.x;
+  const int w = threadIdx.x >> 5, bit = threadIdx.x & 31;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      int e = idx[(long long)t * k + j];
+      e = e < 0 ? 0 : (e >= N ? N - 1 : e);
+      atomicOr(&mask[e * kWords + w], 1u << bit);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < N; e += 256) {
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) c += __popc(mask[e * kWords + i]);
+    blk_counts[(long long)b * N + e] = c;
+  }
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      int e = idx[(long long)t * k + j];
+      e = e < 0 ? 0 : (e >= N ? N - 1 : e);
+      int r = __popc(mask[e * kWords + w] & ((1u << bit) - 1u));
+      for (int i = 0; i < w; ++i) r += __popc(mask[e * kWords + i]);
+      rank[(long long)t * k + j] = r;
+    }
+  }
+}
+
+// One block of 1024 threads: per-expert scan over blocks, then over experts.
+__global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict__ blk_counts,
+                                                            int n_blocks, int N, int T, int k,
+                                                            int with_shared,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets) {
+  __shared__ int32_t tot[kMaxExperts];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < N) {
+    for (int b = 0; b < n_blocks; ++b) {
+      const int c = blk_counts[(long long)b * N + e];
+      blk_counts[(long long)b * N + e] = run;  // becomes the block's base row
+      run += c;
+    }
+    counts[e] = run;
+  }
+  tot[e] = e < N ? run : 0;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over the 1024 totals
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = e >= o ? tot[e - o] : 0;
+    __syncthreads();
+    tot[e] += v;
+    __syncthreads();
+  }
+  if (e < N) offsets[e + 1] = tot[e];
+  if (e == 0) {
+    offsets[0] = 0;
+    offsets[N + 1] = T * k + (with_shared ? T : 0);
+  }
+}
+
+__global__ __launch_bounds__(256) void permute_scatter_kernel(
+    const int32_t* __restrict__ idx, int T, int N, int k, int with_shared,
+    const int32_t* __restrict__ blk_base, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ token_of) {
+  const int t = blockIdx.x * kTokPerBlock + threadIdx.x;
+  if (t >= T) return;
+  const int b = blockIdx.x;
+  for (int j = 0; j < k; ++j) {
+    const long long a = (long long)t * k + j;
+    int e = idx[a];
+    e = e < 0 ? 0 : (e >= N ? N - 1 : e);
+    int row = offsets[e] + blk_base[(long long)b * N + e] + row_of[a];  // row_of holds the rank
+    row = row < 0 ? 0 : (row >= T * k ? T * k - 1 : row);
+    row_of[a] = row;
+    token_of[row] = t;
+  }
+  if (with_shared) token_of[(long long)T * k + t] = t;
+}
+
+}  // namespace
+
+extern "C" size_t moe_permute_workspace_bytes(int T, int N, int k) {
+  (void)k;
+  if (T <= 0 || N <= 0) return 0;
+  const size_t blocks = (size_t)(T + kTokPerBlock - 1) / kTokPerBlock;
+  return blocks * (size_t)N * sizeof(int32_t);
+}
+
+extern "C" moe_status_t moe_permute(const int32_t* topk_idx, int T, int N, int k, int with_shared,
+                                    int32_t* counts, int32_t* offsets, int32_t* row_of,
+                                    int32_t* token_of, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  if (T < 0 || N < 1 || N > kMaxExperts || k < 1 || k > 32) return MOE_ERR_SHAPE;
+  if ((long long)T * (k + 1) > 0x7FFFFFFFLL) return MOE_ERR_SHAPE;
+  if (!counts || !offsets) return MOE_ERR_NULL;
+  if (T > 0 && (!topk_idx || !row_of || !token_of)) return MOE_ERR_NULL;
+  const size_t need = moe_permute_workspace_bytes(T, N, k);
+  if (T > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (moe_status_t s = check_device()) return s;
+  const int n_blocks = (T + kTokPerBlock - 1) / kTokPerBlock;
+  int32_t* blk = static_cast<int32_t*>(ws);
+  if (T > 0)
+    hipLaunchKernelGGL(permute_count_kernel, dim3(n_blocks), dim3(256), 0, stream, topk_idx, T, N,
+                       k, blk, row_of);
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, stream, blk, n_blocks, N, T, k,
+                     with_shared ? 1 : 0, counts, offsets);
+  if (T > 0)
+    hipLaunchKernelGGL(permute_scatter_kernel, dim3(n_blocks), dim3(256), 0, stream, topk_idx, T,
+                       N, k, with_shared ? 1 : 0, blk, offsets, row_of, token_of);
+  return launch_status();
+}

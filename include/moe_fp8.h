@@ -1,0 +1,211 @@
+/*
+ * moe_fp8.h -- C ABI of libmoe_fp8.so: the forward pass of one DeepSeekMoE
+ * layer on an AMD Instinct MI355X (gfx950), FP8 E4M3 with fine-grained scales.
+ *
+ * Pages cited (by title and section):
+ *   [VE] "DeepSeek-V3, explained." (vibeengines.com): numbered recipe steps
+ *        3 (MoE shape), 4 (sigmoid routing with a bias), 5 (no token dropped),
+ *        7 (FP8 with 1x128 / 128x128 scales) and the symbol glossary.
+ *   [TP] "DeepSeek-V3: Auxiliary-Loss-Free MoE Load Balancing, Multi-Token
+ *        Prediction, and FP8 Training at 671B Scale" (trishampatil.com):
+ *        section III (affinity, selection and gate equations; bias thermostat
+ *        and its flowchart), section V (FP8: Figure 6, details 1-4).
+ *   [DF] "DeepSeek-V3 Technical Report" (deepforge.srivtx.xyz): part 1
+ *        "Per-tile FP8 scaling" (scale = 448 / amax, E4M3 rounding).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers on the current HIP device, owned by the
+ *     caller, and must stay valid until the work on `stream` completes.  The
+ *     library never allocates, never synchronises the host and keeps no
+ *     pointer after returning.
+ *   - Matrices are row-major.  Both GEMM operands are K-contiguous.  FP8 values
+ *     are raw OCP E4M3 ("fn", max 448) byte codes.  bf16 values are raw 16-bit
+ *     patterns.  Scales are stored as dequantisation factors d = amax / 448.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream).
+ *   - Return value: MOE_OK, or an error code.  On any code other than
+ *     MOE_ERR_HIP nothing was enqueued.  MOE_ERR_HIP means a HIP launch failed;
+ *     moe_last_hip_error() returns the hipError_t of that failure.
+ *   - Sizes of zero tokens / rows are valid and enqueue nothing.
+ *   - Inputs must be finite; with non-finite inputs output values are
+ *     unspecified but every access stays in bounds.
+ */
+#ifndef MOE_FP8_H
+#define MOE_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  MOE_ERR_SHAPE = 2,       /* a size is negative or violates a divisibility rule */
+  MOE_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned                 */
+  MOE_ERR_WORKSPACE = 4,   /* workspace missing or too small                   */
+  MOE_ERR_DEVICE = 5,      /* the current device is not gfx950                 */
+  MOE_ERR_UNSUPPORTED = 6, /* a valid but unsupported combination of arguments */
+  MOE_ERR_HIP = 7          /* a HIP call failed; see moe_last_hip_error()      */
+} moe_status_t;
+
+typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype_t;
+
+/* Grouped GEMM epilogues. */
+typedef enum {
+  MOE_EPI_BF16 = 0,       /* out: bf16 [total_rows, n_out], row stride ldo elements */
+  MOE_EPI_SWIGLU_FP8 = 1, /* out: E4M3 [total_rows, n_out/2] (ldo bytes per row),
+                             out_d: float [total_rows, n_out/256]                 */
+  MOE_EPI_F32 = 2         /* out: float [total_rows, n_out], row stride ldo       */
+} moe_epilogue_t;
+
+/*
+ * Router and biased top-k ([TP] section III affinity, selection and gate
+ * equations; [VE] recipe step 4):
+ *   s[t,i]   = sigmoid(sum_h x[t,h] * Wr[i,h])       (bf16 inputs, fp32 math)
+ *   chosen   = the k experts with the largest fl32(s[t,i] + bias[i]),
+ *              ties to the lower expert index, listed in that order
+ *   gate[t,j]= s[t,idx[t,j]] / sum_j' s[t,idx[t,j']]  (the bias never enters)
+ * x_bf16 [T,H], w_router_bf16 [N,H] (row i is expert i's centroid), bias [N]
+ * float.  scores [T,N] float is written when non-NULL.  topk_idx int32 [T,k],
+ * topk_gate float [T,k].
+ * Requires H % 128 == 0, 1 <= N <= 256, N % 16 == 0, 1 <= k <= min(N, 32).
+ */
+moe_status_t moe_route_topk(const void* x_bf16, const void* w_router_bf16, const float* bias,
+                            int T, int H, int N, int k, float* scores, int32_t* topk_idx,
+                            float* topk_gate, hipStream_t stream);
+
+/*
+ * The selection and gate steps alone, from a given float score tensor
+ * scores [T,N] (same definitions as moe_route_topk).  Requires 1 <= N <= 1024,
+ * 1 <= k <= min(N, 32).
+ */
+moe_status_t moe_topk_from_scores(const float* scores, const float* bias, int T, int N, int k,
+                                  int32_t* topk_idx, float* topk_gate, hipStream_t stream);
+
+/*
+ * Per-expert token counts and the token permutation.  Every (token, slot)
+ * assignment gets a row; nothing is dropped ([VE] recipe step 5).  The counts
+ * feed the bias update ([TP] section III flowchart, "token counts").
+ *   counts[e]     = #{(t,j): idx[t,j] = e}                       int32 [N]
+ *   offsets[e]    = sum_{e'<e} counts[e'], offsets[N] = T*k,
+ *                   offsets[N+1] = T*k + T if with_shared else T*k   int32 [N+2]
+ *   row_of[t,j]   = offsets[e] + rank of (t,j) among the assignments of e in
+ *                   (token, slot) order                            int32 [T,k]
+ *   token_of[row] = token of that row; with_shared appends group N with rows
+ *                   T*k + t -> t                          int32 [T*k (+T)]
+ * Deterministic (no atomics decide any order).  idx entries must lie in
+ * [0, N) (entries outside are clamped into range).  ws: device scratch of at
+ * least moe_permute_workspace_bytes(T, N, k) bytes.
+ * Requires 1 <= N <= 1024, 1 <= k <= 32.
+ */
+size_t moe_permute_workspace_bytes(int T, int N, int k);
+moe_status_t moe_permute(const int32_t* topk_idx, int T, int N, int k, int with_shared,
+                         int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* token_of,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * 1x128 activation quantiser ([TP] section V FP8 detail 1; [DF] "Per-tile FP8
+ * scaling").  For each row r and 128-column tile j of x [rows, cols] (row
+ * stride ld elements, dtype dt):
+ *   amax = max |x|;  m = fl32(448 / amax);  d[r,j] = fl32(amax / 448);
+ *   q[r,c] = E4M3_RNE_saturating(fl32(x[r,c] * m))    (sign kept)
+ * A tile with amax == 0, or whose m overflows, stores 0x00 codes and d = 1.
+ * q uint8 [rows, cols] (dense), d float [rows, cols/128].
+ * Requires cols % 128 == 0, ld >= cols, ld % 8 == 0.
+ */
+moe_status_t fp8_quant_1x128(const void* x, moe_dtype_t dt, int rows, int cols, int ld,
+                             uint8_t* q, float* d, hipStream_t stream);
+
+/*
+ * 128x128 weight quantiser (same rule per 128x128 block; [VE] recipe step 7).
+ * w_bf16 [batch, rows, cols] -> q uint8 [batch, rows, cols],
+ * d float [batch, rows/128, cols/128].  With interleave_gate_up (for
+ * W1 = [W_gate; W_up], rows = 2I) the output row blocks are reordered so that
+ * output block 2j is gate block j and output block 2j+1 is up block j (d
+ * follows the same order).  Requires rows % 128 == 0, cols % 128 == 0, and
+ * rows % 256 == 0 with interleave_gate_up.
+ */
+moe_status_t fp8_quant_128x128(const void* w_bf16, int batch, int rows, int cols,
+                               int interleave_gate_up, uint8_t* q, float* d, hipStream_t stream);
+
+/*
+ * Grouped block-scaled FP8 GEMM ([TP] section V Figure 6: FP8 inputs, FP32
+ * accumulation, BF16 output; FP8 detail 2: the scales change every 128
+ * elements of K, so each 128-deep block's product is scaled on its own):
+ *   C[r,c] = sum_kb (sum_{h in kb} A[src(r),h] B[g,c,h]) * a_d[src(r),kb] * b_d[g,c/128,kb]
+ * for every row r of group g, i.e. group_offsets[g] <= r < group_offsets[g+1].
+ * src(r) = a_row_index[r] when a_row_index is non-NULL (fused gather), else r.
+ * Epilogues:
+ *   MOE_EPI_BF16        out[r,c] = bf16(C[r,c] * (row_scale ? row_scale[r] : 1))
+ *   MOE_EPI_F32         out[r,c] = C[r,c]
+ *   MOE_EPI_SWIGLU_FP8  B holds W1 with gate/up 128-row blocks interleaved
+ *                       (fp8_quant_128x128 with interleave_gate_up); for h
+ *                       column c' = 128 j + i:  h = SiLU(C[r, 256j+i]) * C[r, 256j+128+i]
+ *                       in float, then 1x128-quantised as fp8_quant_1x128 does:
+ *                       out (E4M3) [r, c'], out_d [r, j].
+ * a_q [a_rows, lda] (lda >= k_dim bytes), a_d [a_rows, k_dim/128]; b_q [G, n_out, k_dim],
+ * b_d [G, n_out/128, k_dim/128]; group_offsets int32 [G+1] on the device,
+ * non-decreasing, group_offsets[0] = 0, group_offsets[G] = total_rows (values
+ * outside [0, total_rows] are clamped).  1 <= num_groups <= 2048.
+ * Requires k_dim % 128 == 0, n_out % 256 == 0, lda % 16 == 0, ldo % 8 == 0
+ * (elements of the output type), 16-byte aligned pointers.
+ */
+typedef struct {
+  const uint8_t* a_q;
+  const float* a_d;
+  int lda;
+  int a_rows;                   /* rows of a_q / a_d; gathered indices are clamped to it */
+  const int32_t* a_row_index;
+  const uint8_t* b_q;
+  const float* b_d;
+  const int32_t* group_offsets;
+  int num_groups;
+  int total_rows;
+  int n_out;
+  int k_dim;
+  int epilogue;
+  void* out;
+  float* out_d;
+  int ldo;
+  const float* row_scale;
+} moe_gemm_fp8_args;
+
+moe_status_t moe_grouped_gemm_fp8(const moe_gemm_fp8_args* args, hipStream_t stream);
+
+/*
+ * Gate-weighted combine ([VE] glossary: routed weights sum to 1 and the shared
+ * expert is added at full weight; [TP] Figure 2, outputs "summed into the
+ * block output"):
+ *   y[t,:] = bf16( residual[t,:] (if non-NULL) + out[shared_row0 + t,:]
+ *                  + sum_{j=0..k-1} gate[t,j] * out[row_of[t,j],:] )
+ * accumulated in float, in that order, one fused multiply-add per slot.
+ * shared_row0 < 0 means no shared expert.  out_rows_bf16 [*, H],
+ * gate float [T,k], row_of int32 [T,k], residual/y bf16 [T,H].
+ * Requires H % 8 == 0.
+ */
+moe_status_t moe_combine(const void* out_rows_bf16, const float* gate, const int32_t* row_of,
+                         int shared_row0, int T, int H, int k, const void* residual_bf16,
+                         void* y_bf16, hipStream_t stream);
+
+/*
+ * Sign-based bias update ([TP] section III, "How the bias is set"; [VE]
+ * recipe step 4): target = T*k/N; overloaded (N*c > T*k) -> b -= gamma,
+ * underloaded (N*c < T*k) -> b += gamma, on target -> unchanged; one float
+ * add of fl32(gamma).  bias float [N] updated in place, counts int32 [N].
+ */
+moe_status_t moe_bias_update(float* bias, const int32_t* counts, int N, int T, int k, float gamma,
+                             hipStream_t stream);
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_str(moe_status_t status);
+/* hipError_t of the most recent MOE_ERR_HIP on this thread (0 if none). */
+int moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP8_H */

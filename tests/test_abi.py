@@ -1,0 +1,102 @@
+"""The C ABI of libmoe_fp8.so, checked on the CPU: the library loads, exports
+every function include/moe_fp8.h declares, and rejects invalid arguments with
+the documented status before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_fp8.h")
+LIB = os.path.join(ROOT, "fp8_block_scaled_sigmoid_amd", "libmoe_fp8.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z][a-z0-9_]+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libmoe_fp8.so is not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_layer_calls():
+    names = declared_functions()
+    for n in ["moe_route_topk", "moe_topk_from_scores", "moe_permute",
+              "moe_permute_workspace_bytes", "fp8_quant_1x128", "fp8_quant_128x128",
+              "moe_grouped_gemm_fp8", "moe_combine", "moe_bias_update", "moe_status_str",
+              "moe_last_hip_error"]:
+        assert n in names, n
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in moe_fp8.h but not exported"
+
+
+def test_status_strings(lib):
+    lib.moe_status_str.restype = ctypes.c_char_p
+    lib.moe_status_str.argtypes = [ctypes.c_int]
+    assert lib.moe_status_str(0) == b"MOE_OK"
+    for c in range(1, 8):
+        assert lib.moe_status_str(c).startswith(b"MOE_ERR_")
+
+
+def test_validation_before_any_launch(lib):
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.moe_permute.argtypes = [P, I, I, I, I, P, P, P, P, P, ctypes.c_size_t, P]
+    # N out of range, k out of range -> shape error
+    assert lib.moe_permute(None, 4, 0, 2, 1, None, None, None, None, None, 0, None) == 2
+    assert lib.moe_permute(None, 4, 8, 33, 1, None, None, None, None, None, 0, None) == 2
+    dummy = ctypes.c_void_p(16)
+    # missing workspace
+    assert lib.moe_permute(dummy, 4, 8, 2, 1, dummy, dummy, dummy, dummy, None, 0, None) == 4
+    lib.fp8_quant_1x128.argtypes = [P, I, I, I, I, P, P, P]
+    assert lib.fp8_quant_1x128(None, 0, 4, 100, 100, None, None, None) == 2     # cols % 128
+    assert lib.fp8_quant_1x128(None, 0, 0, 128, 128, None, None, None) == 0     # empty: no-op
+    assert lib.fp8_quant_1x128(None, 0, 4, 128, 128, None, None, None) == 1     # NULL
+    assert lib.fp8_quant_1x128(ctypes.c_void_p(8), 0, 4, 128, 128, dummy, dummy, None) == 3
+    lib.moe_route_topk.argtypes = [P, P, P, I, I, I, I, P, P, P, P]
+    assert lib.moe_route_topk(None, None, None, 4, 256, 257, 8, None, None, None, None) == 2
+    assert lib.moe_route_topk(None, None, None, 4, 256, 16, 17, None, None, None, None) == 2
+    assert lib.moe_route_topk(None, None, None, 0, 256, 16, 2, None, None, None, None) == 0
+    lib.moe_combine.argtypes = [P, P, P, I, I, I, I, P, P, P]
+    assert lib.moe_combine(None, None, None, 0, 4, 12, 2, None, None, None) == 2   # H % 8
+    lib.moe_bias_update.argtypes = [P, P, I, I, I, ctypes.c_float, P]
+    assert lib.moe_bias_update(None, None, 4, 1, 1, 0.1, None) == 1
+    lib.moe_permute_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_permute_workspace_bytes.argtypes = [I, I, I]
+    assert lib.moe_permute_workspace_bytes(513, 256, 8) == 3 * 256 * 4
+
+
+class GemmArgs(ctypes.Structure):
+    _fields_ = [("a_q", ctypes.c_void_p), ("a_d", ctypes.c_void_p), ("lda", ctypes.c_int),
+                ("a_rows", ctypes.c_int), ("a_row_index", ctypes.c_void_p),
+                ("b_q", ctypes.c_void_p), ("b_d", ctypes.c_void_p),
+                ("group_offsets", ctypes.c_void_p), ("num_groups", ctypes.c_int),
+                ("total_rows", ctypes.c_int), ("n_out", ctypes.c_int), ("k_dim", ctypes.c_int),
+                ("epilogue", ctypes.c_int), ("out", ctypes.c_void_p), ("out_d", ctypes.c_void_p),
+                ("ldo", ctypes.c_int), ("row_scale", ctypes.c_void_p)]
+
+
+def test_gemm_validation(lib):
+    lib.moe_grouped_gemm_fp8.argtypes = [ctypes.POINTER(GemmArgs), ctypes.c_void_p]
+    assert lib.moe_grouped_gemm_fp8(None, None) == 1
+    a = GemmArgs(16, 16, 256, 8, None, 16, 16, 16, 3, 8, 256, 256, 0, 16, None, 256, None)
+    a.k_dim = 200
+    assert lib.moe_grouped_gemm_fp8(ctypes.byref(a), None) == 2   # K % 128
+    a.k_dim, a.n_out = 256, 384
+    assert lib.moe_grouped_gemm_fp8(ctypes.byref(a), None) == 2   # n_out % 256
+    a.n_out, a.epilogue = 256, 9
+    assert lib.moe_grouped_gemm_fp8(ctypes.byref(a), None) == 6
+    a.epilogue, a.total_rows = 0, 0
+    assert lib.moe_grouped_gemm_fp8(ctypes.byref(a), None) == 0   # nothing to do
+    a.total_rows, a.epilogue, a.out_d = 8, 1, None
+    assert lib.moe_grouped_gemm_fp8(ctypes.byref(a), None) == 1   # SwiGLU needs out_d

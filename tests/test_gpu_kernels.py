@@ -1,0 +1,412 @@
+"""GPU parity of each C entry point against the CPU oracle, on the same seeded
+inputs.  Integer results (codes, indices, maps, counts, bias) must match bit
+for bit; float results within the stated tolerances."""
+import numpy as np
+import pytest
+
+import synth
+from helpers import (bf16_from_dev, bf16_to_dev, bf16_values, codes_agree_up_to_ties,
+                     device_tensor, log, rel_l2, to_dev)
+from oracle import bias as obias
+from oracle import e4m3, ffn, permute as opermute, quant, route
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    import fp8_block_scaled_sigmoid_amd as moe
+    moe.lib()
+    return moe
+
+
+def _moe():
+    import fp8_block_scaled_sigmoid_amd as moe
+    return moe
+
+
+# --------------------------------------------------------------------------- generator
+
+
+@pytest.mark.parametrize("name", ["tiny", "prefill", "skew"])
+def test_device_generator_matches_host(name):
+    w = synth.WORKLOADS[name]
+    rows = np.array([0, 1, 7, w.T - 1])
+    log(f"synth x {name}")
+    x = device_tensor(w.x_spec(), w.seed)
+    got = bf16_from_dev(x)[rows]
+    assert np.array_equal(got, synth.generate(w.x_spec(), w.seed, rows=rows))
+    spec = w.wr_spec()
+    t = device_tensor(spec, w.seed)
+    assert np.array_equal(bf16_from_dev(t), synth.generate(spec, w.seed))
+    bspec = synth.Spec(synth.T_BIAS, (w.N,), synth.UNIFORM, 0.05, dtype="f32")
+    tb = device_tensor(bspec, w.seed, dtype="f32")
+    assert np.array_equal(tb.cpu().numpy(), synth.generate(bspec, w.seed))
+
+
+# --------------------------------------------------------------------------- quantisers
+
+
+def _adversarial_rows(H):
+    """Rows exercising the zero-tile, overflow, sign-of-zero and subnormal rules."""
+    rows = np.zeros((6, H), np.float32)
+    rows[1, :] = -0.0
+    rows[2, :128] = np.float32(1e-37)               # fl32(448 / amax) overflows
+    rows[3, :128] = np.linspace(-3e-38, 3e-38, 128)  # tiny, with float32 subnormals
+    rows[3, 5] = np.float32(2e-36)
+    rows[4, :] = np.where(np.arange(H) % 2, 448.0, -448.0)
+    rows[5, :] = np.linspace(-1, 1, H)
+    rows[5, 17] = 1e4                                # outlier in tile 0
+    return rows
+
+
+@pytest.mark.parametrize("name,rows", [("tiny", None), ("decode", None), ("prefill", 37)])
+def test_quant_1x128_bf16_bit_exact(name, rows):
+    moe = _moe()
+    w = synth.WORKLOADS[name]
+    r = np.arange(w.T if rows is None else rows)
+    bits = synth.generate(w.x_spec(), w.seed, rows=r)
+    adv = synth.f32_to_bf16_bits(_adversarial_rows(w.H))
+    bits = np.concatenate([bits, adv])
+    log(f"fp8_quant_1x128 bf16 {name} rows={bits.shape[0]}")
+    q, d = moe.fp8_quant_1x128(bf16_to_dev(bits))
+    torch.cuda.synchronize()
+    wq, wd = quant.quant_1x128(synth.as_f64(bits))
+    assert np.array_equal(q.cpu().numpy(), wq)
+    assert np.array_equal(d.cpu().numpy(), wd)
+
+
+def test_quant_1x128_f32_encoder_sweep():
+    """Tiles whose amax is 448 have m = d = 1, so every other element's code is
+    the E4M3 encoding of that very float: sweep float32 values up to 448 plus
+    every rounding tie and its neighbours, both signs."""
+    moe = _moe()
+    bits = np.arange(0, 0x43E00000, 97, dtype=np.uint64).astype(np.uint32)
+    sweep = bits.view(np.float32)
+    pos = e4m3.POS_VALUES
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    near = [mids]
+    for dirn in (np.inf, -np.inf):
+        cur = mids
+        for _ in range(2):
+            cur = np.nextafter(cur, np.float32(dirn))
+            near.append(cur)
+    vals = np.concatenate([sweep] + near)
+    vals = np.concatenate([vals, -vals])
+    vals = vals[np.abs(vals) <= 448.0]
+    per = 127
+    n_t = (vals.size + per - 1) // per
+    pad = np.zeros(n_t * per, np.float32)
+    pad[:vals.size] = vals
+    tiles = np.concatenate([np.full((n_t, 1), 448.0, np.float32), pad.reshape(n_t, per)], 1)
+    x = tiles.reshape(-1, 1024) if tiles.size % 1024 == 0 else np.concatenate(
+        [tiles.reshape(-1), np.full((-tiles.size) % 1024, 448.0, np.float32)]).reshape(-1, 1024)
+    log(f"fp8_quant_1x128 f32 encoder sweep values={vals.size}")
+    q, d = moe.fp8_quant_1x128(to_dev(x))
+    torch.cuda.synchronize()
+    assert np.all(d.cpu().numpy() == 1.0)
+    assert np.array_equal(q.cpu().numpy(), e4m3.encode(x.astype(np.float64)))
+
+
+def test_quant_1x128_f32_random_tiles():
+    moe = _moe()
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((300, 512)) * np.exp(rng.uniform(-20, 20, (300, 1)))).astype(np.float32)
+    log("fp8_quant_1x128 f32 random")
+    q, d = moe.fp8_quant_1x128(to_dev(x))
+    torch.cuda.synchronize()
+    wq, wd = quant.quant_1x128(x.astype(np.float64))
+    assert np.array_equal(q.cpu().numpy(), wq) and np.array_equal(d.cpu().numpy(), wd)
+
+
+@pytest.mark.parametrize("interleave", [False, True])
+def test_quant_128x128_bit_exact(interleave):
+    moe = _moe()
+    w = synth.WORKLOADS["tiny"]
+    bits = synth.generate(w.w1_spec(), w.seed)          # [17, 256, 256]
+    bits[3, 130, 200] = synth.f32_to_bf16_bits(np.array([7.0], np.float32))[0]   # outlier block
+    bits[4, :128, :128] = 0                                                       # zero block
+    log(f"fp8_quant_128x128 interleave={interleave}")
+    q, d = moe.fp8_quant_128x128(bf16_to_dev(bits), interleave_gate_up=interleave)
+    torch.cuda.synchronize()
+    wq, wd = quant.quant_128x128(synth.as_f64(bits))
+    if interleave:                    # row blocks (gate j, up j) -> (2j, 2j+1)
+        nb = bits.shape[1] // 128
+        order = np.array([j // 2 if j % 2 == 0 else nb // 2 + j // 2 for j in range(nb)])
+        wq = wq.reshape(w.G, nb, 128, -1)[:, order].reshape(wq.shape)
+        wd = wd[:, order]
+    assert np.array_equal(q.cpu().numpy(), wq) and np.array_equal(d.cpu().numpy(), wd)
+
+
+# --------------------------------------------------------------------------- routing
+
+
+@pytest.mark.parametrize("T,N,k,ties", [(1000, 16, 2, False), (777, 256, 8, False),
+                                        (500, 256, 8, True), (64, 1000, 32, False),
+                                        (300, 32, 32, False), (129, 48, 1, True)])
+def test_topk_from_scores_bit_exact(T, N, k, ties):
+    moe = _moe()
+    rng = np.random.default_rng(T + N + k)
+    s = rng.uniform(0, 1, (T, N)).astype(np.float32)
+    b = rng.uniform(-0.05, 0.05, N).astype(np.float32)
+    if ties:
+        s = (np.round(s * 8) / 8).astype(np.float32)
+        b[:] = 0
+    log(f"moe_topk_from_scores T={T} N={N} k={k}")
+    idx, gate = moe.moe_topk_from_scores(to_dev(s), to_dev(b), k)
+    torch.cuda.synchronize()
+    want = route.select_topk(s, b, k)
+    assert np.array_equal(idx.cpu().numpy(), want)
+    g = route.gates(s, want)
+    np.testing.assert_allclose(gate.cpu().numpy(), g, rtol=2e-6, atol=1e-7)
+
+
+def _route_check(x_bits, wr_bits, b, k, s_gpu, idx_gpu, gate_gpu, delta=3e-5):
+    """Scores within 1e-5 of the float64 oracle; indices bit-exact on every
+    token whose k-th/(k+1)-th key gap exceeds delta (three times the score
+    tolerance), a valid top-k of the float64 keys on the others."""
+    s64 = route.router_scores(synth.as_f64(x_bits), synth.as_f64(wr_bits))
+    err = np.max(np.abs(s_gpu - s64))
+    print(f"max |score - oracle| = {err:.3e}")
+    assert err < 1e-5
+    margin = route.topk_margin(s64, b, k)
+    idx_o = route.select_topk(s64.astype(np.float32), b, k)
+    clear = margin > delta
+    assert clear.mean() > 0.97
+    assert np.array_equal(idx_gpu[clear], idx_o[clear])
+    # low-margin tokens: the GPU's set is still a valid top-k of the float64 keys
+    key = s64 + b.astype(np.float64)[None, :]
+    for t in np.nonzero(~clear)[0]:
+        kth = -np.sort(-key[t])[k - 1]
+        assert np.all(key[t, idx_gpu[t]] >= kth - 2 * delta)
+    g = route.gates(s64.astype(np.float32), idx_gpu)
+    np.testing.assert_allclose(gate_gpu, g, rtol=1e-5, atol=1e-6)
+    return int((~clear).sum())
+
+
+@pytest.mark.parametrize("name,T", [("tiny", None), ("routing", 2048), ("prefill", 1000),
+                                    ("skew", 512)])
+def test_route_topk(name, T):
+    moe = _moe()
+    w = synth.WORKLOADS[name]
+    T = w.T if T is None else T
+    xb = synth.generate(w.x_spec(), w.seed, rows=np.arange(T))
+    wrb = w.router_weight()
+    b = w.bias()
+    log(f"moe_route_topk {name} T={T}")
+    idx, gate, s = moe.moe_route_topk(bf16_to_dev(xb), bf16_to_dev(wrb), to_dev(b), w.k)
+    torch.cuda.synchronize()
+    _route_check(xb, wrb, b, w.k, s.cpu().numpy(), idx.cpu().numpy(), gate.cpu().numpy())
+    # scores buffer is optional
+    idx2, gate2, _ = moe.moe_route_topk(bf16_to_dev(xb), bf16_to_dev(wrb), to_dev(b), w.k,
+                                        scores=False)
+    assert torch.equal(idx, idx2) and torch.equal(gate, gate2)
+
+
+def test_route_topk_ragged_small():
+    """T not a multiple of the 32-token tile, N = k (all chosen), N = 16."""
+    moe = _moe()
+    rng = np.random.default_rng(5)
+    for T, H, N, k in [(33, 128, 16, 16), (70, 384, 32, 3), (1, 256, 16, 1)]:
+        x = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+        wr = synth.f32_to_bf16_bits((rng.standard_normal((N, H)) * 0.05).astype(np.float32))
+        b = rng.uniform(-0.1, 0.1, N).astype(np.float32)
+        log(f"moe_route_topk ragged T={T} H={H} N={N} k={k}")
+        idx, gate, s = moe.moe_route_topk(bf16_to_dev(x), bf16_to_dev(wr), to_dev(b), k)
+        torch.cuda.synchronize()
+        _route_check(x, wr, b, k, s.cpu().numpy(), idx.cpu().numpy(), gate.cpu().numpy())
+
+
+# --------------------------------------------------------------------------- permutation
+
+
+@pytest.mark.parametrize("T,N,k,shared", [(1, 16, 1, True), (255, 16, 2, True),
+                                          (256, 256, 8, True), (257, 256, 8, False),
+                                          (4097, 1000, 8, True), (3000, 64, 32, True),
+                                          (16384, 256, 8, True)])
+def test_permute_bit_exact(T, N, k, shared):
+    moe = _moe()
+    rng = np.random.default_rng(T * 7 + N)
+    n_use = N - 5 if N >= 64 else N              # leave some experts empty
+    allowed = rng.permutation(N)[:n_use]
+    idx = allowed[np.argsort(rng.uniform(size=(T, n_use)), axis=1)[:, :k]].astype(np.int32)
+    log(f"moe_permute T={T} N={N} k={k} shared={shared}")
+    c, o, r, t = moe.moe_permute(to_dev(idx), N, shared)
+    torch.cuda.synchronize()
+    wc, wo, wr, wt = opermute.permute(idx, N, shared)
+    assert np.array_equal(c.cpu().numpy(), wc)
+    assert np.array_equal(o.cpu().numpy(), wo)
+    assert np.array_equal(r.cpu().numpy(), wr)
+    assert np.array_equal(t.cpu().numpy(), wt)
+
+
+# --------------------------------------------------------------------------- grouped GEMM
+
+
+def _ragged_offsets(sizes):
+    return np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+
+
+def _int_codes(rng, shape, lim=4):
+    return e4m3.encode(rng.integers(-lim, lim + 1, shape).astype(np.float64))
+
+
+@pytest.mark.parametrize("K,n_out,sizes,gather", [
+    (256, 256, [0, 1, 127, 128, 129, 300, 0], False),
+    (7168, 512, [5, 0, 200], True),
+    (2048, 7168, [130, 3], False),
+])
+def test_gemm_integer_operands_bit_exact(K, n_out, sizes, gather):
+    """Integer-valued codes with power-of-two scales: every partial sum is an
+    exact integer, so the result is exact for any summation order."""
+    moe = _moe()
+    rng = np.random.default_rng(K + n_out)
+    off = _ragged_offsets(sizes)
+    R, G = int(off[-1]), len(sizes)
+    a_rows = R + 13
+    aq = _int_codes(rng, (a_rows, K))
+    ad = np.full((a_rows, K // 128), 2.0 ** -3, np.float32)
+    bq = _int_codes(rng, (G, n_out, K))
+    bd = np.full((G, n_out // 128, K // 128), 2.0 ** -5, np.float32)
+    rix = rng.integers(0, a_rows, R).astype(np.int32) if gather else None
+    src = rix if gather else np.arange(R)
+    want = np.zeros((R, n_out))
+    for g in range(G):
+        rr = np.arange(off[g], off[g + 1])
+        if rr.size:
+            want[rr] = ffn.block_scaled_gemm(aq[src[rr]], ad[src[rr]], bq[g], bd[g])
+    for epi in (moe.MOE_EPI_F32, moe.MOE_EPI_BF16):
+        log(f"moe_grouped_gemm_fp8 integer K={K} n_out={n_out} sizes={sizes} epi={epi}")
+        out, _ = moe.moe_grouped_gemm_fp8(to_dev(aq), to_dev(ad), to_dev(bq), to_dev(bd),
+                                          to_dev(off), R, epi,
+                                          a_row_index=to_dev(rix) if gather else None)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        ref = want if epi == moe.MOE_EPI_F32 else ffn.bf16_round(want)
+        assert np.array_equal(got, ref)
+
+
+def _random_codes(rng, shape):
+    c = rng.integers(0, 256, shape).astype(np.uint8)
+    return np.where((c & 0x7F) == 0x7F, c & 0xF0, c).astype(np.uint8)   # no NaN codes
+
+
+def test_gemm_random_operands_f32():
+    moe = _moe()
+    rng = np.random.default_rng(11)
+    sizes = [17, 0, 260, 128, 1]
+    off = _ragged_offsets(sizes)
+    R, G, K, n_out = int(off[-1]), len(sizes), 1024, 512
+    aq = _random_codes(rng, (R, K))
+    ad = rng.uniform(1e-3, 1e-2, (R, K // 128)).astype(np.float32)
+    bq = _random_codes(rng, (G, n_out, K))
+    bd = rng.uniform(1e-3, 1e-2, (G, n_out // 128, K // 128)).astype(np.float32)
+    log("moe_grouped_gemm_fp8 random f32")
+    out, _ = moe.moe_grouped_gemm_fp8(to_dev(aq), to_dev(ad), to_dev(bq), to_dev(bd),
+                                      to_dev(off), R, moe.MOE_EPI_F32)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    for g in range(G):
+        rr = slice(off[g], off[g + 1])
+        if off[g + 1] > off[g]:
+            want = ffn.block_scaled_gemm(aq[rr], ad[rr], bq[g], bd[g])
+            scale = np.abs(ffn.block_scaled_gemm(aq[rr] & 0x7F, ad[rr], bq[g] & 0x7F, bd[g]))
+            assert np.all(np.abs(got[rr] - want) <= 1e-6 * scale + 1e-30)
+
+
+def test_gemm_swiglu_epilogue():
+    moe = _moe()
+    rng = np.random.default_rng(12)
+    H, I = 512, 256
+    sizes = [40, 0, 130, 7]
+    off = _ragged_offsets(sizes)
+    R, G = int(off[-1]), len(sizes)
+    T = 50
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    xq, xd = quant.quant_1x128(synth.as_f64(xb))
+    w1 = synth.f32_to_bf16_bits((rng.standard_normal((G, 2 * I, H)) * 0.02).astype(np.float32))
+    w1q_nat, w1d_nat = quant.quant_128x128(synth.as_f64(w1))
+    tok = rng.integers(0, T, R).astype(np.int32)
+    log("moe_grouped_gemm_fp8 swiglu")
+    w1q, w1d = moe.fp8_quant_128x128(bf16_to_dev(w1), interleave_gate_up=True)
+    hq, hd = moe.moe_grouped_gemm_fp8(to_dev(xq), to_dev(xd), w1q, w1d, to_dev(off), R,
+                                      moe.MOE_EPI_SWIGLU_FP8, a_row_index=to_dev(tok))
+    torch.cuda.synchronize()
+    hq, hd = hq.cpu().numpy(), hd.cpu().numpy()
+    n_ties = 0
+    for g in range(G):
+        rr = np.arange(off[g], off[g + 1])
+        if not rr.size:
+            continue
+        a = ffn.block_scaled_gemm(xq[tok[rr]], xd[tok[rr]], w1q_nat[g], w1d_nat[g])
+        a32 = ffn.fl32(a)
+        h = ffn.fl32(ffn.silu32(a32[:, :I]) * a32[:, I:])
+        wq, wd = quant.quant_1x128(h)
+        np.testing.assert_allclose(hd[rr], wd, rtol=1e-5)
+        amax = np.abs(h).reshape(rr.size, I // 128, 128).max(-1)
+        m = np.repeat(448.0 / amax, 128, axis=1)
+        n_ties += codes_agree_up_to_ties(hq[rr], wq, h * m)
+    assert n_ties <= 0.001 * R * I
+
+
+# --------------------------------------------------------------------------- combine, bias
+
+
+@pytest.mark.parametrize("T,H,k,shared", [(64, 256, 2, True), (300, 7168, 8, True),
+                                          (5, 4096, 1, False)])
+def test_combine(T, H, k, shared):
+    moe = _moe()
+    rng = np.random.default_rng(T + H)
+    R = T * k + (T if shared else 0)
+    spec = synth.Spec(synth.T_ROWS, (R, H), synth.NORMAL, 0.05)
+    rows_b = synth.generate(spec, 1)
+    gate = rng.uniform(0.01, 1, (T, k)).astype(np.float32)
+    gate /= gate.sum(1, keepdims=True)
+    row_of = rng.permutation(T * k).reshape(T, k).astype(np.int32)
+    log(f"moe_combine T={T} H={H} k={k}")
+    y = moe.moe_combine(bf16_to_dev(rows_b), to_dev(gate), to_dev(row_of),
+                        T * k if shared else -1)
+    torch.cuda.synchronize()
+    got = bf16_values(y)
+    want = ffn.combine(synth.as_f64(rows_b), gate.astype(np.float64), row_of,
+                       T * k if shared else -1, "Q")
+    ulp = np.abs(want) * 2.0 ** -7 + 1e-30
+    diff = np.abs(got - want)
+    assert np.all(diff <= ulp)
+    assert np.mean(diff > 0) < 1e-3
+
+
+def test_combine_with_residual():
+    moe = _moe()
+    rng = np.random.default_rng(9)
+    T, H, k = 16, 256, 2
+    rows = synth.f32_to_bf16_bits(rng.standard_normal((T * k + T, H)).astype(np.float32))
+    res = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    gate = np.full((T, k), 0.5, np.float32)
+    row_of = np.arange(T * k).reshape(T, k).astype(np.int32)
+    y = moe.moe_combine(bf16_to_dev(rows), to_dev(gate), to_dev(row_of), T * k,
+                        residual=bf16_to_dev(res))
+    torch.cuda.synchronize()
+    r = synth.as_f64(rows)
+    acc = ffn.fl32(synth.as_f64(res) + r[T * k:])
+    for j in range(k):
+        acc = ffn.fl32(acc + 0.5 * r[row_of[:, j]])
+    assert np.array_equal(bf16_values(y), ffn.bf16_round(acc))
+
+
+def test_bias_update_bit_exact():
+    moe = _moe()
+    rng = np.random.default_rng(13)
+    for N, T, k, gamma in [(16, 64, 2, 1e-3), (256, 8192, 8, 1e-3), (256, 512, 8, 0.0),
+                           (100, 7, 3, 0.01)]:
+        b = rng.uniform(-0.05, 0.05, N).astype(np.float32)
+        c = rng.integers(0, 2 * T * k // N + 2, N).astype(np.int32)
+        c[:3] = T * k // N if (T * k) % N == 0 else c[:3]
+        bt = to_dev(b.copy())
+        log(f"moe_bias_update N={N}")
+        moe.moe_bias_update(bt, to_dev(c), T, k, gamma)
+        torch.cuda.synchronize()
+        assert np.array_equal(bt.cpu().numpy(), obias.bias_update(b, c, T, k, gamma))

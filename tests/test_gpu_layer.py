@@ -1,0 +1,230 @@
+"""End-to-end parity of the layer (MoELayer.forward, the path bench.py times)
+against the CPU oracle.
+
+Bars: routing indices, counts, permutation maps, FP8 activation codes and the
+bias update bit-exact (routing on tokens whose top-k gap is clear of the
+router's float32 error); the intermediate h codes equal except at rounding
+ties; the output within relative L2 1e-3 of the rounding-faithful oracle
+("Q") and within normwise max relative error 2e-2 of the float64 oracle on the
+same dequantised FP8 operands ("D").
+
+At the DeepSeek-V3 shape (H 7168, 256 routed experts top-8 plus 1 shared,
+I 2048) the oracle recomputes a sample the CPU can afford: all routing, and
+the expert FFN of the least and most loaded routed experts plus a slice of
+the shared expert's rows; the combine and bias update are checked there as
+properties of the GPU's own intermediates.
+"""
+import numpy as np
+import pytest
+
+import synth
+from helpers import (bf16_from_dev, bf16_to_dev, bf16_values, codes_agree_up_to_ties,
+                     device_tensor, log, max_rel, rel_l2, to_dev)
+from oracle import ffn, layer as olayer, quant, route
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _moe():
+    import fp8_block_scaled_sigmoid_amd as moe
+    return moe
+
+
+def _run_small(w, x_bits=None):
+    moe = _moe()
+    x_b = synth.generate(w.x_spec(), w.seed) if x_bits is None else x_bits
+    wr_b = w.router_weight()
+    w1_b = synth.generate(w.w1_spec(), w.seed)
+    w2_b = synth.generate(w.w2_spec(), w.seed)
+    b = w.bias()
+    log(f"layer {w.name} T={w.T} H={w.H} N={w.N} k={w.k} I={w.I}")
+    weights = moe.MoEWeights(bf16_to_dev(wr_b), to_dev(b.copy()), w1_bf16=bf16_to_dev(w1_b),
+                             w2_bf16=bf16_to_dev(w2_b))
+    lay = moe.MoELayer(weights, w.T, w.k, w.gamma)
+    y = bf16_values(lay.forward(bf16_to_dev(x_b)))
+    torch.cuda.synchronize()
+    args = (synth.as_f64(x_b), synth.as_f64(wr_b), b, synth.as_f64(w1_b), synth.as_f64(w2_b),
+            w.k, w.gamma)
+    return lay, weights, y, args
+
+
+def _check_small(lay, weights, y, args, k):
+    q = olayer.moe_layer(*args, precision="Q")
+    s64 = q["s64"]
+    margin = route.topk_margin(s64, args[2], k)
+    assert np.all(margin > 3e-5), "inputs too close to a routing tie for an exact check"
+    assert np.array_equal(lay.idx.cpu().numpy(), q["idx"])
+    assert np.array_equal(lay.counts.cpu().numpy(), q["counts"])
+    assert np.array_equal(lay.offsets.cpu().numpy(), q["offsets"])
+    assert np.array_equal(lay.row_of.cpu().numpy(), q["row_of"])
+    assert np.array_equal(lay.token_of.cpu().numpy(), q["token_of"])
+    assert np.array_equal(lay.xq.cpu().numpy(), q["xq"])
+    assert np.array_equal(lay.xd.cpu().numpy(), q["xd"])
+    np.testing.assert_allclose(lay.gate.cpu().numpy(), q["gate"], rtol=1e-5, atol=1e-6)
+    assert np.array_equal(weights.bias.cpu().numpy(), q["bias"])
+    # h codes: equal except at rounding ties
+    hq = lay.hq.cpu().numpy()
+    I = hq.shape[1]
+    n_h = 0
+    for g in range(q["offsets"].size - 1):
+        r0, r1 = q["offsets"][g], q["offsets"][g + 1]
+        if r1 == r0:
+            continue
+        res = olayer.expert_rows(q["xq"], q["xd"], q["token_of"][r0:r1],
+                                 {kk: q[kk] for kk in ("w1q", "w1d", "w2q", "w2d")}, g, "Q")
+        amax = np.abs(res["h"]).reshape(r1 - r0, I // 128, 128).max(-1)
+        n_h += codes_agree_up_to_ties(hq[r0:r1], res["hq"],
+                                      res["h"] * np.repeat(448.0 / amax, 128, 1))
+    assert n_h <= 1e-3 * hq.size
+    err_q = rel_l2(y, q["y"])
+    d = olayer.moe_layer(*args, precision="D")
+    err_d = max_rel(y, d["y"])
+    print(f"rel L2 vs Q = {err_q:.3e}, normwise max rel vs D = {err_d:.3e}, h ties = {n_h}")
+    assert err_q <= 1e-3
+    assert err_d <= 2e-2
+
+
+def test_layer_tiny():
+    w = synth.WORKLOADS["tiny"]
+    _check_small(*_run_small(w), w.k)
+
+
+@pytest.mark.parametrize("T,H,N,k,I", [(300, 512, 32, 4, 256), (40, 256, 16, 1, 128),
+                                       (17, 384, 16, 16, 128), (1, 256, 16, 2, 128)])
+def test_layer_small_variants(T, H, N, k, I):
+    w = synth.Workload(f"v{T}", T=T, H=H, N=N, k=k, I=I, x_std=1.0, wr_dist=synth.NORMAL,
+                       wr_param=0.05, bias_half=0.1, w_std=0.02, seed=T)
+    lay, weights, y, args = _run_small(w)
+    s64 = route.router_scores(args[0], args[1])
+    if not np.all(route.topk_margin(s64, args[2], k) > 3e-5):
+        pytest.skip("seed gives a routing tie within the router's float32 error")
+    _check_small(lay, weights, y, args, k)
+
+
+def test_layer_zero_input():
+    w = synth.WORKLOADS["tiny"]
+    zero = np.zeros((w.T, w.H), np.uint16)
+    lay, weights, y, args = _run_small(w, zero)
+    assert np.all(y == 0.0)
+    assert np.all(lay.xq.cpu().numpy() == 0) and np.all(lay.xd.cpu().numpy() == 1.0)
+
+
+# --------------------------------------------------------------------------- V3 shape
+
+
+def _build_v3(w):
+    """Weights generated and quantised on the device (22.6 GB of bf16 never
+    reaches the host); the host regenerates the sampled experts only."""
+    moe = _moe()
+    log(f"v3 weights {w.name}")
+    w1 = device_tensor(w.w1_spec(), w.seed)
+    w1q, w1d = moe.fp8_quant_128x128(w1, interleave_gate_up=True)
+    del w1
+    w2 = device_tensor(w.w2_spec(), w.seed)
+    w2q, w2d = moe.fp8_quant_128x128(w2)
+    del w2
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    wr_b = w.router_weight()
+    b = w.bias()
+    weights = moe.MoEWeights(bf16_to_dev(wr_b), to_dev(b.copy()), w1q=w1q, w1d=w1d, w2q=w2q,
+                             w2d=w2d)
+    return weights, wr_b, b
+
+
+def _expert_oracle(w, g):
+    H, I = w.H, w.I
+    w1 = synth.as_f64(synth.generate(w.w1_spec(), w.seed,
+                                     rows=np.arange(g * 2 * I, (g + 1) * 2 * I)))
+    w2 = synth.as_f64(synth.generate(w.w2_spec(), w.seed, rows=np.arange(g * H, (g + 1) * H)))
+    w1q, w1d = quant.quant_128x128(w1)
+    w2q, w2d = quant.quant_128x128(w2)
+    return w1q, w1d, w2q, w2d
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_layer_v3_shape_sampled(name):
+    moe = _moe()
+    w = synth.WORKLOADS[name]
+    weights, wr_b, b0 = _build_v3(w)
+    lay = moe.MoELayer(weights, w.T, w.k, w.gamma)
+    x = device_tensor(w.x_spec(), w.seed)
+    log(f"v3 forward {name}")
+    y = lay.forward(x)
+    torch.cuda.synchronize()
+    idx = lay.idx.cpu().numpy()
+    gate = lay.gate.cpu().numpy()
+    counts = lay.counts.cpu().numpy()
+    offsets = lay.offsets.cpu().numpy()
+    row_of = lay.row_of.cpu().numpy()
+    token_of = lay.token_of.cpu().numpy()
+    T, k, N = w.T, w.k, w.N
+
+    # routing on a token sample, in the oracle's own precision
+    sample = np.arange(T) if T <= 2048 else np.sort(np.random.default_rng(0).choice(T, 2048, False))
+    xb = synth.generate(w.x_spec(), w.seed, rows=sample)
+    assert np.array_equal(bf16_from_dev(x[torch.from_numpy(sample).cuda()]), xb)
+    s64 = route.router_scores(synth.as_f64(xb), synth.as_f64(wr_b))
+    assert np.max(np.abs(lay.scores.cpu().numpy()[sample] - s64)) < 1e-5
+    clear = route.topk_margin(s64, b0, k) > 3e-5
+    assert clear.mean() > 0.97
+    idx_o = route.select_topk(s64.astype(np.float32), b0, k)
+    assert np.array_equal(idx[sample][clear], idx_o[clear])
+    np.testing.assert_allclose(gate[sample], route.gates(s64.astype(np.float32), idx[sample]),
+                               rtol=1e-5, atol=1e-6)
+    # activation codes on the sample: bit-exact
+    xq_o, xd_o = quant.quant_1x128(synth.as_f64(xb))
+    assert np.array_equal(lay.xq.cpu().numpy()[sample], xq_o)
+    assert np.array_equal(lay.xd.cpu().numpy()[sample], xd_o)
+
+    # permutation: properties of the GPU's own routing (bit-exactness of the
+    # permutation itself is covered at this size by test_permute_bit_exact)
+    assert counts.sum() == T * k and np.array_equal(np.bincount(idx.ravel(), minlength=N), counts)
+    assert np.array_equal(np.sort(row_of.ravel()), np.arange(T * k))
+    assert np.array_equal(token_of[row_of], np.repeat(np.arange(T)[:, None], k, 1))
+    for e in range(N):
+        assert np.all(np.diff(token_of[offsets[e]:offsets[e + 1]]) > 0)
+
+    # expert FFN on sampled experts, compared row by row
+    xq_all = lay.xq.cpu().numpy()
+    xd_all = lay.xd.cpu().numpy()
+    hq = lay.hq.cpu().numpy()
+    out_rows = lay.out_rows
+    live = np.nonzero(counts)[0]
+    experts = [int(live[np.argmin(counts[live])]), int(np.argmax(counts)), N]
+    for g in experts:
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        rows = np.arange(r0, r1) if g < N else np.concatenate([np.arange(r0, r0 + 32),
+                                                               np.arange(r1 - 32, r1)])
+        toks = token_of[rows]
+        # the oracle quantises the rows it needs from the generator's x
+        xr = synth.generate(w.x_spec(), w.seed, rows=toks)
+        xq_r, xd_r = quant.quant_1x128(synth.as_f64(xr))
+        assert np.array_equal(xq_all[toks], xq_r) and np.array_equal(xd_all[toks], xd_r)
+        log(f"oracle expert {g} rows={rows.size}")
+        w1q, w1d, w2q, w2d = _expert_oracle(w, g)
+        resq = ffn.expert_ffn(xq_r, xd_r, w1q, w1d, w2q, w2d, "Q")
+        resd = ffn.expert_ffn(xq_r, xd_r, w1q, w1d, w2q, w2d, "D")
+        amax = np.abs(resq["h"]).reshape(rows.size, w.I // 128, 128).max(-1)
+        codes_agree_up_to_ties(hq[rows], resq["hq"], resq["h"] * np.repeat(448.0 / amax, 128, 1))
+        np.testing.assert_allclose(lay.hd.cpu().numpy()[rows], resq["hd"], rtol=1e-5)
+        got = bf16_values(out_rows[torch.from_numpy(rows).cuda()])
+        eq, ed = rel_l2(got, resq["out"]), max_rel(got, resd["out"])
+        print(f"expert {g}: rows {rows.size}, rel L2 vs Q {eq:.2e}, max rel vs D {ed:.2e}")
+        assert eq <= 1e-3 and ed <= 2e-2
+
+    # combine: y is the shared row plus the gate-weighted routed rows (float
+    # FMA chain in slot order), checked on a token sample
+    ts = np.arange(0, T, max(1, T // 256))
+    ob = bf16_values(out_rows)
+    acc = ob[T * k + ts]
+    for j in range(k):
+        acc = ffn.fl32(acc + ffn.fl32(gate[ts, j])[:, None] * ob[row_of[ts, j]])
+    yv = bf16_values(y)[ts]
+    assert np.all(np.abs(yv - ffn.bf16_round(acc)) <= np.abs(yv) * 2.0 ** -7 + 1e-30)
+    # bias: one float32 step of +-gamma or 0 by the integer load comparison
+    want_b = (b0.astype(np.float64) + np.where(N * counts > T * k, -np.float32(w.gamma),
+              np.where(N * counts < T * k, np.float32(w.gamma), 0.0))).astype(np.float32)
+    assert np.array_equal(weights.bias.cpu().numpy(), want_b)
