@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = p.G;
-  const int n_tiles = p.n_out / BN;
+  const int n_tiles = (p.n_out + BN - 1) / BN;   // the last tile may be 128 wide
 
   // ---- tile list: exclusive prefix of (row tiles x column tiles) per group
   {
@@ -163,9 +163,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     src = clampi(src, 0, p.a_rows - 1);
     sa_src = p.a_d + (long long)src * nkb;
   }
-  const uint8_t* b_src =
-      p.b_q + ((long long)g * p.n_out + (long long)n_tile * BN + lrow_ld) * p.k_dim + lchunk * 16;
-  const long long b_step = 64LL * p.k_dim;
+  // B rows past n_out (a 128-wide last tile) re-read the last row; their
+  // results are never stored
+  const uint8_t* b_grp = p.b_q + (long long)g * p.n_out * p.k_dim + lchunk * 16;
+  int b_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b_off[j] = min(n_tile * BN + lrow_ld + 64 * j, p.n_out - 1) * p.k_dim;
   const int st_a0 = swz(lrow_ld, lchunk), st_a1 = swz(lrow_ld + 64, lchunk);
   const int st_b0 = kABytes + swz(lrow_ld, lchunk);
 
@@ -173,7 +176,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   // block per wave: wn < 2 -> block 0 (gate), wn >= 2 -> block 1 (up))
   const int wm = wave & 1, wn = wave >> 1;
   const int lrow = lane & 15, lk = lane >> 4;
-  const float* bd = p.b_d + ((long long)g * (p.n_out / 128) + 2 * n_tile + (wn >> 1)) * nkb;
+  const int nb_w = min(2 * n_tile + (wn >> 1), p.n_out / 128 - 1);   // this wave's weight block
+  const bool wave_cols = 2 * n_tile + (wn >> 1) < p.n_out / 128;    // false: past n_out
+  const float* bd = p.b_d + ((long long)g * (p.n_out / 128) + nb_w) * nkb;
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -188,10 +193,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     const long long ko = (long long)(kb) * BK;                                      \
     ra0 = *reinterpret_cast<const uint4*>(a_src0 + ko);                             \
     ra1 = *reinterpret_cast<const uint4*>(a_src1 + ko);                             \
-    rb0 = *reinterpret_cast<const uint4*>(b_src + ko);                              \
-    rb1 = *reinterpret_cast<const uint4*>(b_src + b_step + ko);                     \
-    rb2 = *reinterpret_cast<const uint4*>(b_src + 2 * b_step + ko);                 \
-    rb3 = *reinterpret_cast<const uint4*>(b_src + 3 * b_step + ko);                 \
+    rb0 = *reinterpret_cast<const uint4*>(b_grp + b_off[0] + ko);                   \
+    rb1 = *reinterpret_cast<const uint4*>(b_grp + b_off[1] + ko);                   \
+    rb2 = *reinterpret_cast<const uint4*>(b_grp + b_off[2] + ko);                   \
+    rb3 = *reinterpret_cast<const uint4*>(b_grp + b_off[3] + ko);                   \
     if (tid < BM) rsa = sa_src[kb];                                                 \
   }
 #define MOE_LSTORE(st)                                                              \
@@ -340,7 +345,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     for (int j = 0; j < 8; ++j) {
       const int q = tid + kThreads * j;
       const int row = q >> 5, c = q & 31;
-      if (m0 + row < rows_g)
+      if (m0 + row < rows_g && n_tile * BN + c * 8 < p.n_out)
         *reinterpret_cast<uint4*>(out + (long long)(row0 + m0 + row) * p.ldo + n_tile * BN + c * 8) =
             *reinterpret_cast<const uint4*>(otile + row * 256 + c * 8);
     }
@@ -351,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = wm * 64 + mi * 16 + 4 * lk + v;
-        if (m0 + row < rows_g) {
+        if (m0 + row < rows_g && wave_cols) {
 #pragma unroll
           for (int ni = 0; ni < 4; ++ni)
             out[(long long)(row0 + m0 + row) * p.ldo + n_tile * BN + wn * 64 + ni * 16 + lrow] =
@@ -370,7 +375,7 @@ moe_status_t launch(const GemmParams& p, hipStream_t stream) {
     if (e != hipSuccess) return hip_fail(e);
     attr_set = true;
   }
-  const long long n_tiles = p.n_out / BN;
+  const long long n_tiles = (p.n_out + BN - 1) / BN;
   long long grid = ((long long)(p.total_rows + BM - 1) / BM + p.G) * n_tiles;
   grid = (grid + 7) / 8 * 8;
   if (grid > 0x7FFFFFFFLL) return MOE_ERR_SHAPE;
@@ -383,11 +388,12 @@ moe_status_t launch(const GemmParams& p, hipStream_t stream) {
 extern "C" moe_status_t moe_grouped_gemm_fp8(const moe_gemm_fp8_args* a, hipStream_t stream) {
   if (!a) return MOE_ERR_NULL;
   if (a->num_groups < 1 || a->num_groups > kMaxGroups || a->total_rows < 0 || a->n_out <= 0 ||
-      a->k_dim <= 0 || a->k_dim % BK != 0 || a->n_out % BN != 0 || a->lda < a->k_dim ||
+      a->k_dim <= 0 || a->k_dim % BK != 0 || a->n_out % 128 != 0 || a->lda < a->k_dim ||
       a->lda % 16 != 0 || a->a_rows < 0)
     return MOE_ERR_SHAPE;
   if (a->epilogue != MOE_EPI_BF16 && a->epilogue != MOE_EPI_SWIGLU_FP8 && a->epilogue != MOE_EPI_F32)
     return MOE_ERR_UNSUPPORTED;
+  if (a->epilogue == MOE_EPI_SWIGLU_FP8 && a->n_out % BN != 0) return MOE_ERR_SHAPE;
   if (a->total_rows == 0) return MOE_OK;
   if (a->a_rows == 0) return MOE_ERR_SHAPE;
   if (!a->a_q || !a->a_d || !a->b_q || !a->b_d || !a->group_offsets || !a->out) return MOE_ERR_NULL;

@@ -65,15 +65,16 @@ def near_tie(scaled, rel=2e-5):
     return d <= rel * np.maximum(a, 2.0 ** -9)
 
 
-def codes_agree_up_to_ties(got, want, scaled_oracle):
-    """E4M3 codes must be equal except where the oracle value sits on a tie;
-    there the two codes must be neighbours."""
+def codes_agree_up_to_ties(got, want, scaled_oracle, rel=2e-5):
+    """E4M3 codes must be equal except where the oracle value lies within
+    `rel` (relative) of a rounding tie; there the two codes must be
+    neighbours.  Returns the number of differing codes."""
     got = np.asarray(got).astype(np.int64)
     want = np.asarray(want).astype(np.int64)
     diff = got != want
     if not diff.any():
         return 0
-    tie = near_tie(scaled_oracle)
+    tie = near_tie(scaled_oracle, rel)
     bad = diff & ~tie
     assert not bad.any(), f"{bad.sum()} codes differ away from a rounding tie"
     from oracle import e4m3
@@ -82,3 +83,24 @@ def codes_agree_up_to_ties(got, want, scaled_oracle):
     ok = np.abs(vg - vw) <= np.maximum(np.abs(vw), np.abs(vg)) * 0.125 + 2.0 ** -9
     assert ok.all(), "codes at a tie differ by more than one step"
     return int(diff.sum())
+
+
+def check_h(hq, hd, h, max_frac=5e-2):
+    """The re-quantised intermediate h of the FP8 GEMM path against the
+    oracle's h (float64 [rows, I]).  The GPU's h carries the MFMA block-sum
+    error (~1e-5 of sum|a*b|), so instead of exact codes: the scales within
+    5e-4, every dequantised value within half an E4M3 step of h plus 1e-3 of
+    its tile maximum, and at most `max_frac` of the codes different.  Returns
+    the number of differing codes."""
+    from oracle import quant
+    rows, I = h.shape
+    wq, wd = quant.quant_1x128(h)
+    np.testing.assert_allclose(hd, wd, rtol=5e-4)
+    amax = np.abs(h).reshape(rows, I // 128, 128).max(-1)
+    hh = quant.dequant_1x128(hq, hd)
+    dd = np.repeat(np.asarray(hd, np.float64), 128, 1)
+    band = 2.0 ** -4 * np.abs(h) + 2.0 ** -10 * dd + 1e-3 * np.repeat(amax, 128, 1)
+    assert np.all(np.abs(hh - h) <= band), "dequantised h outside the E4M3 + MFMA band"
+    n = int(np.sum(np.asarray(hq) != wq))
+    assert n <= max_frac * wq.size, f"{n} of {wq.size} h codes differ"
+    return n

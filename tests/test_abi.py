@@ -92,8 +92,11 @@ def test_gemm_validation(lib):
     a = GemmArgs(16, 16, 256, 8, None, 16, 16, 16, 3, 8, 256, 256, 0, 16, None, 256, None)
     a.k_dim = 200
     assert lib.moe_grouped_gemm_fp8(ctypes.byref(a), None) == 2   # K % 128
-    a.k_dim, a.n_out = 256, 384
-    assert lib.moe_grouped_gemm_fp8(ctypes.byref(a), None) == 2   # n_out % 256
+    a.k_dim, a.n_out = 256, 320
+    assert lib.moe_grouped_gemm_fp8(ctypes.byref(a), None) == 2   # n_out % 128
+    a.n_out, a.epilogue, a.out_d = 384, 1, 16
+    assert lib.moe_grouped_gemm_fp8(ctypes.byref(a), None) == 2   # SwiGLU needs n_out % 256
+    a.out_d = None
     a.n_out, a.epilogue = 256, 9
     assert lib.moe_grouped_gemm_fp8(ctypes.byref(a), None) == 6
     a.epilogue, a.total_rows = 0, 0

@@ -3,10 +3,21 @@ against the CPU oracle.
 
 Bars: routing indices, counts, permutation maps, FP8 activation codes and the
 bias update bit-exact (routing on tokens whose top-k gap is clear of the
-router's float32 error); the intermediate h codes equal except at rounding
-ties; the output within relative L2 1e-3 of the rounding-faithful oracle
-("Q") and within normwise max relative error 2e-2 of the float64 oracle on the
-same dequantised FP8 operands ("D").
+router's float32 error); the output within normwise max relative error 2e-2 of
+the float64 oracle on the same dequantised FP8 operands ("D").
+
+Against the rounding-faithful oracle ("Q": float32 GEMM results, float32
+SwiGLU, bf16 expert outputs, float32 combine) the bar is 1e-3 relative L2
+wherever the two sides share every quantisation decision: GEMM2 + combine fed
+the same h codes (test_gemm2_combine_rounding_faithful).  End to end the two
+sides decide the h codes themselves, and the gfx950 FP8 MFMA sums each group of
+8 products on a grid 2^-13 below the group's largest product
+(test_mfma_block_sum_precision_probe), so about 0.1-0.2 % of the h values land
+on the neighbouring E4M3 code (one step = 6-12 % of that value).  That alone
+moves the output by roughly 0.06 * sqrt(fraction flipped) ~ 1e-3 to 3e-3
+relative L2; the end-to-end bound is therefore E2E_Q_BAR = 5e-3, and the h
+codes are checked separately to stay within half an E4M3 step plus 1e-3 of
+the tile maximum of the oracle's h (check_h).
 
 At the DeepSeek-V3 shape (H 7168, 256 routed experts top-8 plus 1 shared,
 I 2048) the oracle recomputes a sample the CPU can afford: all routing, and
@@ -18,11 +29,15 @@ import numpy as np
 import pytest
 
 import synth
-from helpers import (bf16_from_dev, bf16_to_dev, bf16_values, codes_agree_up_to_ties,
+from helpers import (bf16_from_dev, bf16_to_dev, bf16_values, check_h,
                      device_tensor, log, max_rel, rel_l2, to_dev)
 from oracle import ffn, layer as olayer, quant, route
 
 pytestmark = pytest.mark.gpu
+
+D_BAR = 2e-2        # normwise max relative error vs the float64 oracle
+Q_BAR = 1e-3        # relative L2 vs the rounding-faithful oracle, shared h codes
+E2E_Q_BAR = 5e-3    # relative L2 vs the rounding-faithful oracle, end to end
 
 torch = pytest.importorskip("torch")
 
@@ -64,9 +79,9 @@ def _check_small(lay, weights, y, args, k):
     assert np.array_equal(lay.xd.cpu().numpy(), q["xd"])
     np.testing.assert_allclose(lay.gate.cpu().numpy(), q["gate"], rtol=1e-5, atol=1e-6)
     assert np.array_equal(weights.bias.cpu().numpy(), q["bias"])
-    # h codes: equal except at rounding ties
+    # h: the re-quantised intermediate, within the E4M3 + MFMA band
     hq = lay.hq.cpu().numpy()
-    I = hq.shape[1]
+    hd = lay.hd.cpu().numpy()
     n_h = 0
     for g in range(q["offsets"].size - 1):
         r0, r1 = q["offsets"][g], q["offsets"][g + 1]
@@ -74,16 +89,14 @@ def _check_small(lay, weights, y, args, k):
             continue
         res = olayer.expert_rows(q["xq"], q["xd"], q["token_of"][r0:r1],
                                  {kk: q[kk] for kk in ("w1q", "w1d", "w2q", "w2d")}, g, "Q")
-        amax = np.abs(res["h"]).reshape(r1 - r0, I // 128, 128).max(-1)
-        n_h += codes_agree_up_to_ties(hq[r0:r1], res["hq"],
-                                      res["h"] * np.repeat(448.0 / amax, 128, 1))
-    assert n_h <= 1e-3 * hq.size
+        n_h += check_h(hq[r0:r1], hd[r0:r1], res["h"])
     err_q = rel_l2(y, q["y"])
     d = olayer.moe_layer(*args, precision="D")
     err_d = max_rel(y, d["y"])
-    print(f"rel L2 vs Q = {err_q:.3e}, normwise max rel vs D = {err_d:.3e}, h ties = {n_h}")
-    assert err_q <= 1e-3
-    assert err_d <= 2e-2
+    print(f"rel L2 vs Q = {err_q:.3e}, normwise max rel vs D = {err_d:.3e}, "
+          f"h codes differing = {n_h} of {hq.size}")
+    assert err_q <= E2E_Q_BAR
+    assert err_d <= D_BAR
 
 
 def test_layer_tiny():
@@ -207,13 +220,12 @@ def test_layer_v3_shape_sampled(name):
         w1q, w1d, w2q, w2d = _expert_oracle(w, g)
         resq = ffn.expert_ffn(xq_r, xd_r, w1q, w1d, w2q, w2d, "Q")
         resd = ffn.expert_ffn(xq_r, xd_r, w1q, w1d, w2q, w2d, "D")
-        amax = np.abs(resq["h"]).reshape(rows.size, w.I // 128, 128).max(-1)
-        codes_agree_up_to_ties(hq[rows], resq["hq"], resq["h"] * np.repeat(448.0 / amax, 128, 1))
-        np.testing.assert_allclose(lay.hd.cpu().numpy()[rows], resq["hd"], rtol=1e-5)
+        n_h = check_h(hq[rows], lay.hd.cpu().numpy()[rows], resq["h"])
         got = bf16_values(out_rows[torch.from_numpy(rows).cuda()])
         eq, ed = rel_l2(got, resq["out"]), max_rel(got, resd["out"])
-        print(f"expert {g}: rows {rows.size}, rel L2 vs Q {eq:.2e}, max rel vs D {ed:.2e}")
-        assert eq <= 1e-3 and ed <= 2e-2
+        print(f"expert {g}: rows {rows.size}, rel L2 vs Q {eq:.2e}, max rel vs D {ed:.2e}, "
+              f"h codes differing {n_h}")
+        assert eq <= E2E_Q_BAR and ed <= D_BAR
 
     # combine: y is the shared row plus the gate-weighted routed rows (float
     # FMA chain in slot order), checked on a token sample
@@ -228,3 +240,37 @@ def test_layer_v3_shape_sampled(name):
     want_b = (b0.astype(np.float64) + np.where(N * counts > T * k, -np.float32(w.gamma),
               np.where(N * counts < T * k, np.float32(w.gamma), 0.0))).astype(np.float32)
     assert np.array_equal(weights.bias.cpu().numpy(), want_b)
+
+
+@pytest.mark.parametrize("T,H,N,k,I", [(64, 256, 16, 2, 128), (200, 1024, 8, 3, 512),
+                                       (48, 7168, 4, 2, 2048)])
+def test_gemm2_combine_rounding_faithful(T, H, N, k, I):
+    """GEMM2 + combine fed the same h codes on both sides (codes made by the
+    oracle's quantiser from generated values): the rounding-faithful bar."""
+    moe = _moe()
+    rng = np.random.default_rng(T + H)
+    idx = np.argsort(rng.uniform(size=(T, N)), 1)[:, :k].astype(np.int32)
+    from oracle import permute as opermute
+    counts, offsets, row_of, token_of = opermute.permute(idx, N, True)
+    R = T * k + T
+    h = synth.as_f64(synth.generate(synth.Spec(synth.T_ROWS, (R, I), synth.NORMAL, 0.3), T))
+    hq, hd = quant.quant_1x128(h)
+    w2 = synth.generate(synth.Spec(synth.T_W2, (N + 1, H, I), synth.NORMAL, 0.006), T)
+    w2q, w2d = quant.quant_128x128(synth.as_f64(w2))
+    gate = rng.uniform(0.05, 1, (T, k)).astype(np.float32)
+    gate /= gate.sum(1, keepdims=True)
+    log(f"gemm2+combine T={T} H={H} N={N} k={k} I={I}")
+    out, _ = moe.moe_grouped_gemm_fp8(to_dev(hq), to_dev(hd), to_dev(w2q), to_dev(w2d),
+                                      to_dev(offsets), R, moe.MOE_EPI_BF16)
+    y = moe.moe_combine(out, to_dev(gate), to_dev(row_of), T * k)
+    torch.cuda.synchronize()
+    want_out = np.zeros((R, H))
+    for g in range(N + 1):
+        rr = slice(offsets[g], offsets[g + 1])
+        if offsets[g + 1] > offsets[g]:
+            want_out[rr] = ffn.bf16_round(ffn.block_scaled_gemm(hq[rr], hd[rr], w2q[g], w2d[g]))
+    want_y = ffn.combine(want_out, gate.astype(np.float64), row_of, T * k, "Q")
+    err_out = rel_l2(bf16_values(out), want_out)
+    err = rel_l2(bf16_values(y), want_y)
+    print(f"rel L2: expert rows {err_out:.3e}, y {err:.3e}")
+    assert err_out <= Q_BAR and err <= Q_BAR
