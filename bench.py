@@ -34,6 +34,9 @@ def parse():
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "decode", "skew", "routing", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also time a plain 2 GiB device copy (reference for the HBM "
+                         "byte counters and the measured copy bandwidth)")
     return ap.parse_args()
 
 
@@ -208,6 +211,21 @@ def main():
         "weight_quant_ms": round(t_wq1 + t_wq2, 3),
         "wall_s_timed": round(wall, 3),
     }
+    if args.copy_calibration:
+        n = 1 << 31
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        res["copy_calibration"] = {"bytes_read": n, "bytes_written": n, "ms": round(ms, 4),
+                                   "GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+        del src, dst
     if not args.no_cpu_baseline and w.with_experts:
         res["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(res))

@@ -23,6 +23,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # float division and sqrt correctly rounded (448 / amax must be exact)
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # MFMA results in VGPRs: the per-block scale FMA reads them directly
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     "-I", INCLUDE, "-I", CSRC,
 ]

@@ -149,7 +149,8 @@ moe_status_t fp8_quant_128x128(const void* w_bf16, int batch, int rows, int cols
  * a_q [a_rows, lda] (lda >= k_dim bytes), a_d [a_rows, k_dim/128]; b_q [G, n_out, k_dim],
  * b_d [G, n_out/128, k_dim/128]; group_offsets int32 [G+1] on the device,
  * non-decreasing, group_offsets[0] = 0, group_offsets[G] = total_rows (values
- * outside [0, total_rows] are clamped).  1 <= num_groups <= 2048.
+ * outside [0, total_rows] are clamped).  1 <= num_groups <= 1025, k_dim <= 16384,
+ * a_rows * lda < 2^31 (MOE_ERR_UNSUPPORTED otherwise).
  * Requires k_dim % 128 == 0, n_out % 128 == 0 (% 256 with MOE_EPI_SWIGLU_FP8),
  * lda % 16 == 0, ldo % 8 == 0 elements (% 16 bytes for SWIGLU_FP8), 16-byte
  * aligned a_q, b_q and out.
