@@ -24,6 +24,38 @@ import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
+# rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the GEMM1 kernel at this
+# workload; its bytes count only while the kernel source is unchanged
+COUNTERS = os.path.join(ROOT, "profiles", "layer_prefill_T8192_hbm_counters.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "fp8_block_scaled_sigmoid_amd", "csrc", f)
+                  for f in ("gemm_fp8.hip", "common.h")]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per GEMM1 launch from the committed counter summary, or None
+    if there is none for this workload or the kernel changed since."""
+    if workload != "prefill" or not os.path.exists(COUNTERS):
+        return None
+    vals = {}
+    for line in open(COUNTERS):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            vals[key.strip()] = val.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch_calibrated"])
+    except (KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -40,16 +72,16 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(w, sample_tokens=1024):
+def cpu_baseline(w, sample_tokens=None):
     """The oracle, untuned, on a bounded sample of the same workload.
 
-    Sample: the first `sample_tokens` tokens of the batch.  Routing, the
-    activation quantisation, the permutation, the combine and the bias update
-    run on the whole sample; the expert FFN runs on every sample row of the
-    shared expert and of the two routed experts with the most sample rows, and
-    its per-row time is scaled to the sample's T*(k+1) rows (the per-row cost
-    of the FFN does not depend on which expert the row belongs to).  Result:
-    tokens per second of the whole layer on the host."""
+    Sample: the first `sample_tokens` tokens of the batch (default: all of
+    it).  Routing, the activation quantisation, the permutation, the combine
+    and the bias update run on the whole sample; the expert FFN runs on every
+    sample row of the shared expert and of the two routed experts with the
+    most sample rows, and its per-row time is scaled to the sample's T*(k+1)
+    rows (the per-row cost of the FFN does not depend on which expert the row
+    belongs to).  Result: tokens per second of the whole layer on the host."""
     import synth
     from oracle import bias as obias, ffn, permute as operm, quant, route
     try:
@@ -57,7 +89,7 @@ def cpu_baseline(w, sample_tokens=1024):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
-    S = min(sample_tokens, w.T)
+    S = w.T if sample_tokens is None else min(sample_tokens, w.T)
     x = synth.as_f64(synth.generate(w.x_spec(), w.seed, rows=np.arange(S)))
     wr = synth.as_f64(w.router_weight())
     b = w.bias()
@@ -176,15 +208,53 @@ def main():
             per[n].append(a.elapsed_time(b))
     kern = {n: float(np.mean(v)) for n, v in per.items()}
 
-    R = w.R
-    g1_flops = 2.0 * R * w.H * 2 * w.I
-    g2_flops = 2.0 * R * w.I * w.H
+    R, G, T, H, I = w.R, w.G, w.T, w.H, w.I
+    g1_flops = 2.0 * R * H * 2 * I
+    g2_flops = 2.0 * R * I * H
+    # algorithmic HBM bytes of one GEMM1 launch: every W1 code and scale once,
+    # every token's x codes and scales once, the row map, h codes and scales out
+    g1_bytes = (G * 2 * I * H + G * (2 * I // 128) * (H // 128) * 4
+                + T * H + T * (H // 128) * 4 + R * 4 + (G + 1) * 4
+                + R * I + R * (I // 128) * 4)
+    t_g1 = kern["gemm1"] * 1e-3
     gemm_tflops = (g1_flops + g2_flops) / ((kern["gemm1"] + kern["gemm2"]) * 1e-3) / 1e12
-    g1_tflops = g1_flops / (kern["gemm1"] * 1e-3) / 1e12
+    g1_tflops = g1_flops / t_g1 / 1e12
+    g1_gbs = g1_bytes / t_g1 / 1e9
+    # the binding roof is the one with the longer minimum time
+    hbm_bound = g1_bytes / (HBM_PEAK_GBS * 1e9) >= g1_flops / (FP8_PEAK_TFLOPS * 1e12)
     tokens_per_s = w.T / (ms_step * 1e-3)
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(g1_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(g1_tflops, 2), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(g1_tflops / FP8_PEAK_TFLOPS, 4)}
+    roof.update({"traffic": measured_traffic(args.workload),
+                 "kernel": "grouped_gemm_kernel<SWIGLU_FP8> (GEMM1)",
+                 "kernel_avg_ms": round(kern["gemm1"], 4),
+                 "algorithmic_bytes_per_launch": g1_bytes,
+                 "algorithmic_flops_per_launch": g1_flops,
+                 "mfma_tflops": round(g1_tflops, 2),
+                 "mfma_frac": round(g1_tflops / FP8_PEAK_TFLOPS, 4),
+                 "hbm_gbs": round(g1_gbs, 1),
+                 "hbm_frac": round(g1_gbs / HBM_PEAK_GBS, 4)})
+
+    # the HBM-bound phases: algorithmic bytes (each input read once, each output
+    # written once) over the measured kernel time
+    N, k = w.N, w.k
+    phase_bytes = {
+        "route": T * H * 2 + N * H * 2 + N * 4 + T * N * 4 + T * k * 8,
+        "quant_x": T * H * 2 + T * H + T * (H // 128) * 4,
+        "combine": R * H * 2 + T * k * 8 + T * H * 2,
+        "permute": T * k * 4 + N * 4 + (N + 2) * 4 + T * k * 4 + R * 4,
+    }
+    phases = {n: {"bytes": b, "ms": round(kern[n], 4),
+                  "GBps": round(b / (kern[n] * 1e-3) / 1e9, 1),
+                  "hbm_frac": round(b / (kern[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+              for n, b in phase_bytes.items()}
 
     res = {
-        "metric": "MoE layer tokens/s (DeepSeek-V3 shape, FP8 block-scaled, 1 GPU)",
+        "metric": "MoE layer tokens/s + grouped FP8 GEMM TFLOP/s (% peak) at V3 shape, 1 GPU",
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -200,14 +270,11 @@ def main():
                                f"top-{w.k} + 1 shared, SwiGLU intermediate {w.I}, FP8 E4M3 "
                                f"1x128 / 128x128 scales",
                    "T": w.T, "H": w.H, "N": w.N, "k": w.k, "I": w.I},
-        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_kernel<SWIGLU_FP8> (GEMM1)",
-                     "achieved": round(g1_tflops, 2), "peak": FP8_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(g1_tflops / FP8_PEAK_TFLOPS, 4),
-                     "traffic": None,
-                     "algorithmic_flops_per_launch": g1_flops},
+        "roofline": roof,
         "gemm_tflops": round(gemm_tflops, 2),
         "gemm_frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
         "kernel_ms": {n: round(v, 4) for n, v in kern.items()},
+        "hbm_phases": phases,
         "weight_quant_ms": round(t_wq1 + t_wq2, 3),
         "wall_s_timed": round(wall, 3),
     }
