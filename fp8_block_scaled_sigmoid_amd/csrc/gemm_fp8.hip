@@ -38,6 +38,8 @@
 //     tile) are mapped to the same XCD so their weight tile is fetched from HBM
 //     once and re-read from that XCD's L2; row subtiles past the end of a
 //     group's rows skip their MFMAs.
+#include <type_traits>
+
 #include "common.h"
 
 namespace {
@@ -84,11 +86,18 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-__device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)l, 16, 0, 0);
+// Direct-to-LDS copies through a buffer resource: the per-lane byte offset is
+// fixed for the whole K loop and the K position is the scalar offset, so
+// issuing a copy costs no vector instructions.  Offsets past num_records read
+// as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
-__device__ __forceinline__ void dma4(const void* g, uint8_t* l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)l, 4, 0, 0);
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int voff, int soff, uint8_t* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)l, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, int voff, int soff, uint8_t* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)l, 4, voff, soff, 0, 0);
 }
 
 // Wait until at most N of this wave's direct-to-LDS loads are outstanding and
@@ -106,7 +115,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   __shared__ int s_tmp[kThreads];
   __shared__ float s_bd[2][kMaxKb];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.G;
   const int n_tiles = (p.n_out + BN - 1) / BN;   // the last tile may be 128 wide
 
@@ -161,7 +171,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     const int mid = (lo + hi) >> 1;
     if (s_prefix[mid] <= L) lo = mid; else hi = mid;
   }
-  const int g = lo;
+  const int g = __builtin_amdgcn_readfirstlane(lo);
   const int row0 = clampi(p.offsets[g], 0, p.total_rows);
   const int rows_g = clampi(p.offsets[g + 1], 0, p.total_rows) - row0;
   const int mt = (rows_g + BM - 1) / BM;
@@ -185,6 +195,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   // is the same for every j of this lane.
   const int chunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
   const int lrow8 = 8 * wave + (lane >> 3);            // row inside each 64-row band
+  const int nkb_all = p.k_dim / BK;
+  const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(p.a_q, (int)(p.a_rows * p.lda));
+  const __amdgpu_buffer_rsrc_t rs_sa = make_rsrc(p.a_d, p.a_rows * nkb_all * 4);
   int a_off[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -198,22 +211,36 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     const int r = row0 + min(m0 + 64 * wave + lane, rows_g - 1);
     int src = p.a_row_index ? p.a_row_index[r] : r;
     src = clampi(src, 0, p.a_rows - 1);
-    sa_off = src * nkb;
+    sa_off = src * nkb_all * 4;
   }
-  const uint8_t* b_tile = p.b_q + ((long long)g * p.n_out + (long long)n_tile * BN) * p.k_dim;
-  const int b_lane = lrow8 * p.k_dim + chunk * 16;
-  const int b_band = 64 * p.k_dim;                     // 64 rows
+  const int b_rows = half_tile ? 128 : BN;
+  const __amdgpu_buffer_rsrc_t rs_b =
+      make_rsrc(p.b_q + ((long long)g * p.n_out + (long long)n_tile * BN) * p.k_dim, b_rows * p.k_dim);
+  int b_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int jj = half_tile ? (j & 1) : j;             // past n_out: repeat valid rows
+    b_off[j] = (lrow8 + 64 * jj) * p.k_dim + chunk * 16;
+  }
 
-  auto issue = [&](int kb, uint8_t* st) {
+  // the copies of one stage, in four parts so they can be spread over a K
+  // block's MFMAs: part 0 the A tile, parts 1-2 the B tile, part 3 the A scales
+  auto issue_part = [&](int kb, uint8_t* st, int part) {
     const int ko = kb * BK;
+    if (part == 0) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) dma16(p.a_q + a_off[j] + ko, st + (8 * j + wave) * 1024);
+      for (int j = 0; j < 2; ++j) dma16(rs_a, a_off[j], ko, st + (8 * j + wave) * 1024);
+    } else if (part < 3) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int jj = half_tile ? (j & 1) : j;             // past n_out: repeat valid rows
-      dma16(b_tile + b_lane + jj * b_band + ko, st + kABytes + (8 * j + wave) * 1024);
+      for (int j = 2 * part - 2; j < 2 * part; ++j)
+        dma16(rs_b, b_off[j], ko, st + kABytes + (8 * j + wave) * 1024);
+    } else if (wave < 2) {
+      dma4(rs_sa, sa_off, kb * 4, st + kABytes + kBBytes + wave * 256);
     }
-    if (wave < 2) dma4(p.a_d + sa_off + kb, st + kABytes + kBBytes + wave * 256);
+  };
+  auto issue = [&](int kb, uint8_t* st) {
+#pragma unroll
+    for (int part = 0; part < 4; ++part) issue_part(kb, st, part);
   };
 
   // ---- wave tile: rows wm*64..+64, B-tile rows wn*64..+64; wn < 2 lies in
@@ -229,66 +256,83 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue(0, smem);
-  if (nkb > 1) issue(1, smem + kStage);
-  for (int kb = 0; kb < nkb; ++kb) {
-    // stage kb must have landed; stage kb + 1 may still be in flight
-    if (kb + 1 < nkb) {
-      if (wave < 2) wait_and_barrier<7>(); else wait_and_barrier<6>();
-    } else {
-      wait_and_barrier<0>();
-    }
-    if (kb + 2 < nkb) issue(kb + 2, smem + ((kb + 2) % kStages) * kStage);
-    if (wave_rows > 0 && wave_cols) {
-      // every operand of this K block first (the reads overlap each other),
-      // then 16 MFMAs with the scale FMAs of column subtile ni - 1 issued
-      // behind the MFMAs of subtile ni, so no FMA waits on a fresh result
+  // The K loop, for a wave whose first NMI 16-row subtiles hold valid rows
+  // (the others are padding of a group's last row tile and skip their MFMAs).
+  auto kloop = [&](auto nmi_c) {
+    constexpr int NMI = decltype(nmi_c)::value;
+    issue(0, smem);
+    if (nkb > 1) issue(1, smem + kStage);
+    for (int kb = 0; kb < nkb; ++kb) {
+      // stage kb must have landed; stage kb + 1 may still be in flight
+      if (kb + 1 < nkb) {
+        if (wave < 2) wait_and_barrier<7>(); else wait_and_barrier<6>();
+      } else {
+        wait_and_barrier<0>();
+      }
+      const bool more = kb + 2 < nkb;
+      uint8_t* st_next = smem + ((kb + 2) % kStages) * kStage;
+      if (NMI == 0) {
+        if (more) issue(kb + 2, st_next);
+        continue;
+      }
+      // MFMA lane group lk takes the 16-byte K chunks lk and lk + 4 of its
+      // row, for A and B alike (a fixed permutation of K inside the block,
+      // so the dot product is unchanged); this keeps each ds_read_b128 free
+      // of LDS bank conflicts, which chunks 2 lk and 2 lk + 1 are not.
+      // The A fragments, row scales and the first B fragment are read first;
+      // then for each column subtile ni: the next B fragment is read and one
+      // part of stage kb + 2 is requested while the 4 MFMAs of ni run, with
+      // the scale FMAs of subtile ni - 1 behind them (no FMA waits on a
+      // fresh result).
       const uint8_t* st = smem + (kb % kStages) * kStage;
       const float* sA = reinterpret_cast<const float*>(st + kABytes + kBBytes);
       const float sb = s_bd[wn >> 1][kb];
-      f32x4 sa4[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        sa4[mi] = *reinterpret_cast<const f32x4*>(sA + wm * 64 + mi * 16 + 4 * lk);
-      i32x8 af[4], bfr[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int r = wm * 64 + mi * 16 + lrow;
-        const i32x4 x0 = *reinterpret_cast<const i32x4*>(st + swz(r, 2 * lk));
-        const i32x4 x1 = *reinterpret_cast<const i32x4*>(st + swz(r, 2 * lk + 1));
-        af[mi] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
+      auto read_b = [&](int ni) {
         const int r = wn * 64 + ni * 16 + lrow;
-        const i32x4 y0 = *reinterpret_cast<const i32x4*>(st + kABytes + swz(r, 2 * lk));
-        const i32x4 y1 = *reinterpret_cast<const i32x4*>(st + kABytes + swz(r, 2 * lk + 1));
-        bfr[ni] = __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
+        const i32x4 y0 = *reinterpret_cast<const i32x4*>(st + kABytes + swz(r, lk));
+        const i32x4 y1 = *reinterpret_cast<const i32x4*>(st + kABytes + swz(r, lk + 4));
+        return __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
       f32x4 sc[4];
+      i32x8 af[4], bfr[2];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) sc[mi] = sa4[mi] * sb;
+      for (int mi = 0; mi < NMI; ++mi) {
+        const int r = wm * 64 + mi * 16 + lrow;
+        const i32x4 x0 = *reinterpret_cast<const i32x4*>(st + swz(r, lk));
+        const i32x4 x1 = *reinterpret_cast<const i32x4*>(st + swz(r, lk + 4));
+        af[mi] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+        sc[mi] = *reinterpret_cast<const f32x4*>(sA + wm * 64 + mi * 16 + 4 * lk);
+      }
+      bfr[0] = read_b(0);
+#pragma unroll
+      for (int mi = 0; mi < NMI; ++mi) sc[mi] = sc[mi] * sb;
       f32x4 part[2][4];
 #pragma unroll
       for (int ni = 0; ni < 5; ++ni) {
+        if (ni < 3) bfr[(ni + 1) & 1] = read_b(ni + 1);
+        if (ni < 4 && more) issue_part(kb + 2, st_next, ni);
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
+        for (int mi = 0; mi < NMI; ++mi) {
           if (ni < 4)
             part[ni & 1][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                af[mi], bfr[ni], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                af[mi], bfr[ni & 1], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
           if (ni > 0) {
 #pragma unroll
             for (int v = 0; v < 4; ++v)
               acc[mi][ni - 1][v] =
                   __builtin_fmaf(part[(ni - 1) & 1][mi][v], sc[mi][v], acc[mi][ni - 1][v]);
           }
-          if (ni > 0 && ni < 4) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four FMAs
-          }
         }
       }
     }
+  };
+  const int nmi = wave_cols ? clampi((wave_rows + 15) >> 4, 0, 4) : 0;
+  switch (__builtin_amdgcn_readfirstlane(nmi)) {
+    case 4: kloop(std::integral_constant<int, 4>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    default: kloop(std::integral_constant<int, 0>{}); break;
   }
   __syncthreads();   // every wave is done with the stages before they are reused
 
