@@ -111,7 +111,6 @@ __device__ __forceinline__ void wait_and_barrier() {
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p) {
   extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ int s_prefix[kMaxGroups + 1];
   __shared__ int s_tmp[kThreads];
   __shared__ float s_bd[2][kMaxKb];
 
@@ -120,62 +119,68 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   const int G = p.G;
   const int n_tiles = (p.n_out + BN - 1) / BN;   // the last tile may be 128 wide
 
-  // ---- tile list: exclusive prefix of (row tiles x column tiles) per group
+  // ---- tile list: tiles are ordered (group, column tile, row tile), and
+  // group g owns ceil(rows_g / BM) * n_tiles of them.  Thread t counts the
+  // tiles of groups t * per .. t * per + per - 1 (per <= 3); a wave-level scan
+  // and one pass over the 8 wave totals give every thread the exclusive prefix
+  // of its groups, and the thread whose range holds this workgroup's tile
+  // publishes the group and its first tile.
+  int g, local;
   {
     const int per = (G + kThreads - 1) / kThreads;   // <= 3
     int cnt[3];
     int run = 0;
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-      const int g = tid * per + i;
+      const int gi = tid * per + i;
       int c = 0;
-      if (i < per && g < G) {
-        const int r0 = clampi(p.offsets[g], 0, p.total_rows);
-        const int r1 = clampi(p.offsets[g + 1], 0, p.total_rows);
+      if (i < per && gi < G) {
+        const int r0 = clampi(p.offsets[gi], 0, p.total_rows);
+        const int r1 = clampi(p.offsets[gi + 1], 0, p.total_rows);
         const int rows = r1 > r0 ? r1 - r0 : 0;
         c = ((rows + BM - 1) / BM) * n_tiles;
       }
       cnt[i] = c;
       run += c;
     }
-    s_tmp[tid] = run;
-    __syncthreads();
-    for (int o = 1; o < kThreads; o <<= 1) {
-      const int v = tid >= o ? s_tmp[tid - o] : 0;
-      __syncthreads();
-      s_tmp[tid] += v;
-      __syncthreads();
+    int incl = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
     }
-    int base = s_tmp[tid] - run;
+    if (lane == 63) s_tmp[wave] = incl;
+    __syncthreads();
+    int base = incl - run, total = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+      const int t = s_tmp[w];
+      if (w < wave) base += t;
+      total += t;
+    }
+    // XCD-aware mapping: dispatch sends block b to XCD b % 8; give each XCD
+    // a contiguous run of the tile list.  (total is the same in every thread,
+    // so a workgroup leaves as a whole.)
+    const int per_xcd = (total + 7) / 8;
+    const int slot = blockIdx.x >> 3, xcd = blockIdx.x & 7;
+    const int L = xcd * per_xcd + slot;
+    if (slot >= per_xcd || L >= total) return;
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-      const int g = tid * per + i;
-      if (i < per && g < G) {
-        s_prefix[g] = base;
-        base += cnt[i];
+      const int gi = tid * per + i;
+      if (i < per && gi < G && L >= base && L < base + cnt[i]) {
+        s_tmp[8] = gi;
+        s_tmp[9] = base;
       }
+      base += cnt[i];
     }
-    if (tid == kThreads - 1) s_prefix[G] = s_tmp[tid];
     __syncthreads();
+    g = __builtin_amdgcn_readfirstlane(s_tmp[8]);
+    local = L - s_tmp[9];
   }
-  const int total = s_prefix[G];
-  // XCD-aware mapping: dispatch sends block b to XCD b % 8; give each XCD a
-  // contiguous run of the tile list.
-  const int per_xcd = (total + 7) / 8;
-  const int slot = blockIdx.x >> 3, xcd = blockIdx.x & 7;
-  if (slot >= per_xcd) return;
-  const int L = xcd * per_xcd + slot;
-  if (L >= total) return;
-  int lo = 0, hi = G;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (s_prefix[mid] <= L) lo = mid; else hi = mid;
-  }
-  const int g = __builtin_amdgcn_readfirstlane(lo);
   const int row0 = clampi(p.offsets[g], 0, p.total_rows);
   const int rows_g = clampi(p.offsets[g + 1], 0, p.total_rows) - row0;
   const int mt = (rows_g + BM - 1) / BM;
-  const int local = L - s_prefix[g];
   const int n_tile = local / mt;
   const int m0 = (local - n_tile * mt) * BM;
   const int rows_valid = min(BM, rows_g - m0);
@@ -247,6 +252,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   // weight block 0 (gate), wn >= 2 in block 1 (up)
   const int wm = wave & 1, wn = wave >> 1;
   const int lrow = lane & 15, lk = lane >> 4;
+  // byte offset of this lane's K chunks lk and lk + 4 in row lrow of a
+  // 16-row subtile (swz() of that row and chunk)
+  const int frag_lo = lrow * 128 + ((lk ^ ((lrow >> 1) & 7)) << 4);
+  const int frag_hi = lrow * 128 + (((lk + 4) ^ ((lrow >> 1) & 7)) << 4);
   const int wave_rows = rows_valid - wm * 64;          // <= 0: nothing to compute
   const bool wave_cols = !(half_tile && wn >= 2);
 
@@ -260,20 +269,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   // (the others are padding of a group's last row tile and skip their MFMAs).
   auto kloop = [&](auto nmi_c) {
     constexpr int NMI = decltype(nmi_c)::value;
-    issue(0, smem);
-    if (nkb > 1) issue(1, smem + kStage);
-    for (int kb = 0; kb < nkb; ++kb) {
+    // one K block.  MORE: stage kb + 2 exists and is requested meanwhile;
+    // LAST: no stage follows this one.
+    auto kblock = [&](int kb, auto more_c, auto last_c) {
+      constexpr bool more = decltype(more_c)::value, last = decltype(last_c)::value;
       // stage kb must have landed; stage kb + 1 may still be in flight
-      if (kb + 1 < nkb) {
+      if (!last) {
         if (wave < 2) wait_and_barrier<7>(); else wait_and_barrier<6>();
       } else {
         wait_and_barrier<0>();
       }
-      const bool more = kb + 2 < nkb;
       uint8_t* st_next = smem + ((kb + 2) % kStages) * kStage;
       if (NMI == 0) {
         if (more) issue(kb + 2, st_next);
-        continue;
+        return;
       }
       // MFMA lane group lk takes the 16-byte K chunks lk and lk + 4 of its
       // row, for A and B alike (a fixed permutation of K inside the block,
@@ -284,24 +293,29 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
       // part of stage kb + 2 is requested while the 4 MFMAs of ni run, with
       // the scale FMAs of subtile ni - 1 behind them (no FMA waits on a
       // fresh result).
+      // Subtile rows differ by multiples of 16, so a lane's swizzle term is
+      // the same in every subtile: one lane offset per chunk half, and the
+      // subtiles sit at constant offsets from it.
       const uint8_t* st = smem + (kb % kStages) * kStage;
-      const float* sA = reinterpret_cast<const float*>(st + kABytes + kBBytes);
+      const float* sA = reinterpret_cast<const float*>(st + kABytes + kBBytes) + wm * 64 + 4 * lk;
       const float sb = s_bd[wn >> 1][kb];
+      const uint8_t* a_lo = st + wm * 64 * 128 + frag_lo;
+      const uint8_t* a_hi = st + wm * 64 * 128 + frag_hi;
+      const uint8_t* b_lo = st + kABytes + wn * 64 * 128 + frag_lo;
+      const uint8_t* b_hi = st + kABytes + wn * 64 * 128 + frag_hi;
       auto read_b = [&](int ni) {
-        const int r = wn * 64 + ni * 16 + lrow;
-        const i32x4 y0 = *reinterpret_cast<const i32x4*>(st + kABytes + swz(r, lk));
-        const i32x4 y1 = *reinterpret_cast<const i32x4*>(st + kABytes + swz(r, lk + 4));
+        const i32x4 y0 = *reinterpret_cast<const i32x4*>(b_lo + ni * 16 * 128);
+        const i32x4 y1 = *reinterpret_cast<const i32x4*>(b_hi + ni * 16 * 128);
         return __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
       };
       f32x4 sc[4];
       i32x8 af[4], bfr[2];
 #pragma unroll
       for (int mi = 0; mi < NMI; ++mi) {
-        const int r = wm * 64 + mi * 16 + lrow;
-        const i32x4 x0 = *reinterpret_cast<const i32x4*>(st + swz(r, lk));
-        const i32x4 x1 = *reinterpret_cast<const i32x4*>(st + swz(r, lk + 4));
+        const i32x4 x0 = *reinterpret_cast<const i32x4*>(a_lo + mi * 16 * 128);
+        const i32x4 x1 = *reinterpret_cast<const i32x4*>(a_hi + mi * 16 * 128);
         af[mi] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-        sc[mi] = *reinterpret_cast<const f32x4*>(sA + wm * 64 + mi * 16 + 4 * lk);
+        sc[mi] = *reinterpret_cast<const f32x4*>(sA + mi * 16);
       }
       bfr[0] = read_b(0);
 #pragma unroll
@@ -324,7 +338,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
           }
         }
       }
-    }
+    };
+    issue(0, smem);
+    if (nkb > 1) issue(1, smem + kStage);
+    int kb = 0;
+    for (; kb + 2 < nkb; ++kb) kblock(kb, std::true_type{}, std::false_type{});
+    if (kb + 1 < nkb) kblock(kb++, std::false_type{}, std::false_type{});
+    kblock(kb, std::false_type{}, std::true_type{});
   };
   const int nmi = wave_cols ? clampi((wave_rows + 15) >> 4, 0, 4) : 0;
   switch (__builtin_amdgcn_readfirstlane(nmi)) {
@@ -339,60 +359,64 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   // ---- epilogues.  Lane value (mi, ni, v) sits at tile row
   // wm*64 + mi*16 + 4*lk + v and tile column wn*64 + ni*16 + lrow.
   if (EPI == MOE_EPI_SWIGLU_FP8) {
-    constexpr int ldu = 132;
-    float* upt = reinterpret_cast<float*>(smem);                 // [128][132] up values
-    float* red = reinterpret_cast<float*>(smem + 128 * ldu * 4); // [2][128] row maxima
-    uint8_t* otile = smem + 128 * ldu * 4 + 1024;                // [128][128] codes
-    if (wn >= 2) {
+    // Gate wave (wm, wn < 2) and up wave (wm, wn + 2) hold the same rows and
+    // h columns.  Each hands the other half of its subtiles through LDS (gate
+    // columns 2-3 to the up wave, up columns 0-1 to the gate wave), so all 8
+    // waves form h = SiLU(gate) * up for two column subtiles each.  A row's
+    // 128 h values (one 1x128 tile) then lie in 4 waves; their maxima meet in
+    // LDS.
+    float* ex = reinterpret_cast<float*>(smem);                   // [8 waves][32][64]
+    float* red = reinterpret_cast<float*>(smem + 65536);          // [4][128] row maxima
+    uint8_t* otile = smem + 65536 + 2048;                          // [128][128] codes
+    const bool gate_wave = wn < 2;
+    const int partner = gate_wave ? wave + 4 : wave - 4;           // wn +- 2
+    const int give0 = gate_wave ? 2 : 0;                           // subtiles handed over
+    const int keep0 = gate_wave ? 0 : 2;                           // subtiles kept
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            upt[(wm * 64 + mi * 16 + 4 * lk + v) * ldu + (wn - 2) * 64 + ni * 16 + lrow] =
-                acc[mi][ni][v];
-    }
+        for (int v = 0; v < 4; ++v)
+          ex[(wave * 32 + (mi * 2 + j) * 4 + v) * 64 + lane] = acc[mi][give0 + j][v];
     __syncthreads();
-    float h[4][4][4];
-    if (wn < 2) {
+    float h[4][2][4];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = wm * 64 + mi * 16 + 4 * lk + v;
-          float mx = 0.0f;
+      for (int v = 0; v < 4; ++v) {
+        const int row = wm * 64 + mi * 16 + 4 * lk + v;
+        float mx = 0.0f;
 #pragma unroll
-          for (int ni = 0; ni < 4; ++ni) {
-            const float gt = acc[mi][ni][v];
-            const float u = upt[row * ldu + wn * 64 + ni * 16 + lrow];
-            const float e = expf(-gt);
-            const float sg = 1.0f / (1.0f + e);
-            const float silu = gt * sg;
-            h[mi][ni][v] = silu * u;
-            mx = fmaxf(mx, fabsf(h[mi][ni][v]));
-          }
-          mx = group_max<16>(mx);
-          if (lrow == 0) red[wn * 128 + row] = mx;
+        for (int j = 0; j < 2; ++j) {
+          const float mine = acc[mi][keep0 + j][v];
+          const float other = ex[(partner * 32 + (mi * 2 + j) * 4 + v) * 64 + lane];
+          const float gt = gate_wave ? mine : other;
+          const float u = gate_wave ? other : mine;
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gt));
+          h[mi][j][v] = gt * sg * u;
+          mx = fmaxf(mx, fabsf(h[mi][j][v]));
         }
-    }
+        mx = group_max<16>(mx);
+        if (lrow == 0) red[wn * 128 + row] = mx;
+      }
     __syncthreads();
-    if (wn < 2) {
-      const int ld_d = p.n_out / BN;  // h scale row stride (h has n_out/2 columns)
+    const int ld_d = p.n_out / BN;  // h scale row stride (h has n_out/2 columns)
+    const int hc = (wn & 1) * 64;   // this wave's 64-column half of the h tile
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = wm * 64 + mi * 16 + 4 * lk + v;
-          float m, d;
-          tile_scale(fmaxf(red[row], red[128 + row]), m, d);
+      for (int v = 0; v < 4; ++v) {
+        const int row = wm * 64 + mi * 16 + 4 * lk + v;
+        float m, d;
+        tile_scale(fmaxf(fmaxf(red[row], red[128 + row]), fmaxf(red[256 + row], red[384 + row])),
+                   m, d);
 #pragma unroll
-          for (int ni = 0; ni < 4; ++ni)
-            otile[row * 128 + wn * 64 + ni * 16 + lrow] = (uint8_t)quant_code(h[mi][ni][v], m);
-          if (wn == 0 && lrow == 0 && row < rows_valid)
-            p.out_d[(long long)(row0 + m0 + row) * ld_d + n_tile] = d;
-        }
-    }
+        for (int j = 0; j < 2; ++j)
+          otile[row * 128 + hc + (keep0 + j) * 16 + lrow] = (uint8_t)quant_code(h[mi][j][v], m);
+        if (wn == 0 && lrow == 0 && row < rows_valid)
+          p.out_d[(long long)(row0 + m0 + row) * ld_d + n_tile] = d;
+      }
     __syncthreads();
     uint8_t* out = static_cast<uint8_t*>(p.out);
 #pragma unroll
