@@ -55,7 +55,7 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build()")
         L = ctypes.CDLL(LIB_PATH)
         sig = {
-            "moe_route_topk": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P],
+            "moe_route_topk": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, ctypes.c_size_t, _P],
             "moe_topk_from_scores": [_P, _P, _I, _I, _I, _P, _P, _P],
             "moe_permute": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
             "fp8_quant_1x128": [_P, _I, _I, _I, _I, _P, _P, _P],
@@ -70,6 +70,8 @@ def lib():
             f.restype = ctypes.c_int
         L.moe_permute_workspace_bytes.argtypes = [_I, _I, _I]
         L.moe_permute_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_route_workspace_bytes.argtypes = [_I, _I, _I]
+        L.moe_route_workspace_bytes.restype = ctypes.c_size_t
         L.moe_status_str.argtypes = [_I]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_last_hip_error.argtypes = []
@@ -104,10 +106,15 @@ def _dev(t, dtype, name):
 # the C entry points
 
 
-def moe_route_topk(x, w_router, bias, k, scores=True, idx=None, gate=None, stream=None):
+def moe_route_workspace_bytes(T, H, N):
+    return int(lib().moe_route_workspace_bytes(T, H, N))
+
+
+def moe_route_topk(x, w_router, bias, k, scores=True, idx=None, gate=None, ws=None, stream=None):
     """Sigmoid router + biased top-k.  x [T,H] bf16, w_router [N,H] bf16,
     bias [N] float32.  Returns (idx int32 [T,k], gate float32 [T,k],
-    scores float32 [T,N] or None)."""
+    scores float32 [T,N] or None).  ws: optional uint8 device scratch of
+    moe_route_workspace_bytes(T, H, N) bytes."""
     T, H = x.shape
     N = w_router.shape[0]
     _dev(x, torch.bfloat16, "x"), _dev(w_router, torch.bfloat16, "w_router")
@@ -118,9 +125,12 @@ def moe_route_topk(x, w_router, bias, k, scores=True, idx=None, gate=None, strea
         scores = None
     idx = torch.empty(T, k, dtype=torch.int32, device=x.device) if idx is None else idx
     gate = torch.empty(T, k, dtype=torch.float32, device=x.device) if gate is None else gate
+    if ws is None:
+        ws = torch.empty(max(moe_route_workspace_bytes(T, H, N), 16), dtype=torch.uint8,
+                         device=x.device)
     _check("moe_route_topk", lib().moe_route_topk(_ptr(x), _ptr(w_router), _ptr(bias), T, H, N, k,
-                                                  _ptr(scores), _ptr(idx), _ptr(gate),
-                                                  _stream(stream)))
+                                                  _ptr(scores), _ptr(idx), _ptr(gate), _ptr(ws),
+                                                  ws.numel(), _stream(stream)))
     return idx, gate, scores
 
 
@@ -271,6 +281,8 @@ class MoELayer:
         self.row_of = torch.empty(T, k, dtype=torch.int32, **e)
         self.token_of = torch.empty(R, dtype=torch.int32, **e)
         self.ws = torch.empty(max(moe_permute_workspace_bytes(T, N, k), 16), dtype=torch.uint8, **e)
+        self.route_ws = torch.empty(max(moe_route_workspace_bytes(T, H, N), 16), dtype=torch.uint8,
+                                    **e)
         self.xq = torch.empty(T, H, dtype=torch.uint8, **e)
         self.xd = torch.empty(T, H // 128, dtype=torch.float32, **e)
         self.hq = torch.empty(R, I, dtype=torch.uint8, **e)
@@ -281,7 +293,7 @@ class MoELayer:
     # the individual steps, so that callers can time or replace one of them
     def route(self, x, stream=None):
         moe_route_topk(x, self.w.w_router, self.w.bias, self.k, scores=self.scores, idx=self.idx,
-                       gate=self.gate, stream=stream)
+                       gate=self.gate, ws=self.route_ws, stream=stream)
 
     def permute(self, stream=None):
         moe_permute(self.idx, self.w.N, self.with_shared,

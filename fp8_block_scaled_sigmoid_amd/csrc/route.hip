@@ -6,11 +6,17 @@
 // stays in bf16 with float accumulation, as the pages keep the gating network
 // out of FP8 (same page, section V, FP8 detail 4).
 //
-// moe_route_topk: one workgroup owns 32 tokens and every expert (N <= 256), so
-// a token's whole score row stays on chip: a bf16 MFMA GEMM (16x16x32) over
-// LDS-staged, double-buffered 64-wide K chunks, the sigmoid in the epilogue,
-// then each wave selects the top k of 8 tokens by k rounds of a wave-wide
-// argmax on a (key, -index) composite, which gives ties to the lower index.
+// moe_route_topk in two launches.  The router GEMM x [T,H] . Wr^T [H,N] is
+// split along H into S slices so that about one workgroup per compute unit
+// exists; a workgroup computes the partial logits of 128 tokens x all N
+// experts over its slice with bf16 MFMA (16x16x32) from LDS tiles filled by
+// direct-to-LDS copies three stages deep, and writes them to the workspace.
+// The second launch takes one wave per token: it sums the S partial logits in
+// slice order (so the result does not depend on timing), applies the
+// sigmoid, and selects the top k by k rounds of a wave-wide argmax on a
+// (key, -index) composite, which gives ties to the lower index.
+#include <type_traits>
+
 #include "common.h"
 
 namespace {
@@ -21,9 +27,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBT = 32;    // tokens per workgroup
-constexpr int kKC = 64;    // K chunk, bf16 elements (128 bytes per row)
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 constexpr int kMaxN = 256;
+constexpr int kRT = 128;                        // tokens per workgroup
+constexpr int kRKc = 64;                        // K chunk: 64 bf16 = 128 bytes per row
+constexpr int kRStage = (kRT + kMaxN) * 128;    // 48 KiB: x rows, then Wr rows
+constexpr int kRStages = 3;
+constexpr int kRLds = kRStages * kRStage;       // 144 KiB
+constexpr int kRThreads = 512;                  // 8 waves: 2 token bands x 4 expert bands
 
 __device__ __forceinline__ uint32_t sortable(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -81,139 +93,175 @@ __device__ __forceinline__ void wave_topk(const float (&key)[PER], const float (
 
 __device__ __forceinline__ float sigmoidf_acc(float z) { return 1.0f / (1.0f + expf(-z)); }
 
-// x [T,H] bf16, wr [N,H] bf16, bias [N]; outputs scores [T,N] (optional),
-// idx [T,k], gate [T,k].
-__global__ __launch_bounds__(256) void route_topk_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-    const float* __restrict__ bias, int T, int H, int N, int k, float* __restrict__ scores,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
-  // staging: [2][kBT + kMaxN][kKC] bf16 = 2 * 288 * 128 B = 72 KiB; reused for
-  // the score tile [kBT][kMaxN + 4] float after the K loop
+// Number of H slices for T tokens: enough workgroups for about one per
+// compute unit, at most one slice per 64-wide chunk.
+int route_splits(int T, int H) {
+  const int nc = H / kRKc;
+  const int tiles = (T + kRT - 1) / kRT;
+  int S = (256 + tiles - 1) / tiles;
+  return S < 1 ? 1 : (S > nc ? nc : S);
+}
+
+__device__ __forceinline__ int clampi_dev(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// Wait until at most N of this wave's direct-to-LDS copies are outstanding
+// and its LDS reads are done, then meet the other waves (the compiler does
+// not track the LDS side of these copies).
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Partial router logits: ws[s][t][e] = sum over the H slice s of
+// x[t,h] * Wr[e,h] (bf16 products, float accumulation in the MFMA).
+// Workgroup layout: the (slice, token tile) list is slice-major and each XCD
+// takes a contiguous run of it, so one XCD mostly reads one slice of Wr.
+// LDS rows are 128 B; 16-byte chunk c of row r sits at c ^ ((r >> 1) & 7).
+__global__ __launch_bounds__(kRThreads, 1) void route_partial_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int H, int N, int S,
+    float* __restrict__ ws) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * kBT;
-  // the stage always holds kBT + kMaxN rows; rows past kBT + N repeat the last
-  // expert row and are never read
-  constexpr int stage_bytes = (kBT + kMaxN) * 128;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tiles = (T + kRT - 1) / kRT;
+  const int total = tiles * S;
+  const int per_xcd = (total + 7) / 8;
+  const int slot = blockIdx.x >> 3, xcd = blockIdx.x & 7;
+  const int L = xcd * per_xcd + slot;
+  if (slot >= per_xcd || L >= total) return;
+  const int s = L / tiles, tile = L - s * tiles;
+  const int t0 = tile * kRT;
+  const int nc = H / kRKc;
+  const int c0 = (int)((long long)s * nc / S), c1 = (int)((long long)(s + 1) * nc / S);
+  const int nck = c1 - c0;
 
-  // global chunk assignment: row rr of the stage (x rows first, then wr rows),
-  // 16-byte chunk c (0..7), stored at chunk position c ^ (rr & 7)
-  const uint16_t* src_ptr[9];
-  int dst_off[9];
+  // copies: load j of wave w fills the 1 KiB block 8 j + w of the stage
+  // (rows 64 j + 8 w + (lane >> 3)); x has 2 loads per wave, Wr 4.
+  const int chunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
+  const int lrow8 = 8 * wave + (lane >> 3);
+  const __amdgpu_buffer_rsrc_t rs_x = make_rsrc(x, (int)((long long)T * H * 2));
+  const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(wr, N * H * 2);
+  int x_off[2], w_off[4];
 #pragma unroll
-  for (int i = 0; i < 9; ++i) {
-    const int q = tid + 256 * i;
-    const int rr = q >> 3, c = q & 7;
-    if (rr < kBT) {
-      int t = t0 + rr;
-      t = t < T ? t : T - 1;
-      src_ptr[i] = x + (long long)t * H + c * 8;
-    } else {
-      const int e = rr - kBT < N ? rr - kBT : N - 1;
-      src_ptr[i] = wr + (long long)e * H + c * 8;
-    }
-    dst_off[i] = rr * 128 + ((c ^ (rr & 7)) << 4);
+  for (int j = 0; j < 2; ++j) {
+    const int t = min(t0 + 64 * j + lrow8, T - 1);
+    x_off[j] = t * H * 2 + chunk * 16;
   }
-  const int NS = N >> 4;  // expert subtiles of 16
-  f32x4 acc[2][4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int j = 0; j < 4; ++j) {
+    const int e = min(64 * j + lrow8, N - 1);
+    w_off[j] = e * H * 2 + chunk * 16;
+  }
+  auto issue = [&](int i, uint8_t* st) {
+    const int ko = (c0 + i) * 128;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_x, (lds_ptr_t)(st + (8 * j + wave) * 1024), 16,
+                                               x_off[j], ko, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs_w, (lds_ptr_t)(st + kRT * 128 + (8 * j + wave) * 1024), 16, w_off[j], ko, 0, 0);
+  };
 
-  i32x4 reg[9];
+  // wave tile: tokens wm*64..+64, experts wn*64..+64 (NI valid 16-expert
+  // subtiles); lane l reads row l & 15 of a subtile, K chunk 4 ks + (l >> 4)
+  const int wm = wave & 1, wn = wave >> 1;
+  const int lrow = lane & 15, lk = lane >> 4;
+  const int ni_valid = clampi_dev((N - wn * 64) >> 4, 0, 4);
+  const int sw = (lrow >> 1) & 7;
+  const int frag0 = lrow * 128 + ((lk ^ sw) << 4);         // ks = 0
+  const int frag1 = lrow * 128 + (((lk + 4) ^ sw) << 4);   // ks = 1
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 9; ++i)
-    reg[i] = *reinterpret_cast<const i32x4*>(src_ptr[i]);
+  for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-  for (int i = 0; i < 9; ++i)
-    *reinterpret_cast<i32x4*>(smem + dst_off[i]) = reg[i];
-  __syncthreads();
-  const int nkc = H / kKC;
-  for (int kc = 0; kc < nkc; ++kc) {
-    const int cur = kc & 1;
-    const bool more = kc + 1 < nkc;
-    if (more) {
+    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto kloop = [&](auto ni_c) {
+    constexpr int NI = decltype(ni_c)::value;
+    issue(0, smem);
+    if (nck > 1) issue(1, smem + kRStage);
+    for (int i = 0; i < nck; ++i) {
+      if (i + 1 < nck) wait_and_barrier<6>(); else wait_and_barrier<0>();
+      if (i + 2 < nck) issue(i + 2, smem + ((i + 2) % kRStages) * kRStage);
+      if (NI == 0) continue;
+      const uint8_t* st = smem + (i % kRStages) * kRStage;
 #pragma unroll
-      for (int i = 0; i < 9; ++i)
-        reg[i] = *reinterpret_cast<const i32x4*>(src_ptr[i] + (kc + 1) * kKC);
-    }
-    const uint8_t* sb = smem + cur * stage_bytes;
+      for (int ks = 0; ks < 2; ++ks) {
+        const int fo = ks ? frag1 : frag0;
+        bf16x8 af[4], bfr[NI > 0 ? NI : 1];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {         // two 32-deep MFMA slices
-      const int cpos = 4 * ks + (lane >> 4);  // 16-byte chunk of this lane
-      bf16x8 af[2];
+        for (int mi = 0; mi < 4; ++mi)
+          af[mi] = *reinterpret_cast<const bf16x8*>(st + (wm * 64 + mi * 16) * 128 + fo);
 #pragma unroll
-      for (int ti = 0; ti < 2; ++ti) {
-        const int rr = ti * 16 + (lane & 15);
-        af[ti] = *reinterpret_cast<const bf16x8*>(sb + rr * 128 + ((cpos ^ (rr & 7)) << 4));
+        for (int ni = 0; ni < NI; ++ni)
+          bfr[ni] = *reinterpret_cast<const bf16x8*>(st + (kRT + wn * 64 + ni * 16) * 128 + fo);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int mi = 0; mi < 4; ++mi)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
       }
+    }
+    if (NI == 0) return;
+    // lane value (mi, ni, v): token wm*64 + mi*16 + 4*lk + v, expert
+    // wn*64 + ni*16 + lrow
 #pragma unroll
-      for (int ei = 0; ei < 4; ++ei) {
-        const int es = wave + 4 * ei;
-        if (es < NS) {
-          const int rr = kBT + es * 16 + (lane & 15);
-          const bf16x8 bfr =
-              *reinterpret_cast<const bf16x8*>(sb + rr * 128 + ((cpos ^ (rr & 7)) << 4));
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-          for (int ti = 0; ti < 2; ++ti)
-            acc[ti][ei] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ti], bfr, acc[ti][ei], 0, 0, 0);
+      for (int v = 0; v < 4; ++v) {
+        const int t = t0 + wm * 64 + mi * 16 + 4 * lk + v;
+        if (t < T) {
+          float* row = ws + ((long long)s * T + t) * N + wn * 64 + lrow;
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) row[ni * 16] = acc[mi][ni][v];
         }
       }
-    }
-    uint8_t* nb = smem + (cur ^ 1) * stage_bytes;
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < 9; ++i) *reinterpret_cast<i32x4*>(nb + dst_off[i]) = reg[i];
-    }
-    __syncthreads();
+  };
+  switch (__builtin_amdgcn_readfirstlane(ni_valid)) {
+    case 4: kloop(std::integral_constant<int, 4>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    default: kloop(std::integral_constant<int, 0>{}); break;
   }
+}
 
-  // epilogue: sigmoid -> score tile in LDS (and global)
-  float* sc = reinterpret_cast<float*>(smem);
-  const int ldsc = kMaxN + 4;
+// One wave per token: logits = sum of the S partials in slice order, scores =
+// sigmoid, then the biased top k and the unbiased gates.
+template <int PER>
+__global__ __launch_bounds__(256) void route_finish_kernel(const float* __restrict__ ws, int S,
+                                                           const float* __restrict__ bias, int T,
+                                                           int N, int k, float* __restrict__ scores,
+                                                           int32_t* __restrict__ idx,
+                                                           float* __restrict__ gate) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float key[PER], scr[PER];
 #pragma unroll
-  for (int ei = 0; ei < 4; ++ei) {
-    const int es = wave + 4 * ei;
-    if (es < NS) {
-      const int e = es * 16 + (lane & 15);
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int tl = ti * 16 + 4 * (lane >> 4) + v;
-          const float s = sigmoidf_acc(acc[ti][ei][v]);
-          sc[tl * ldsc + e] = s;
-          if (scores && t0 + tl < T) scores[(long long)(t0 + tl) * N + e] = s;
-        }
-      }
+  for (int p = 0; p < PER; ++p) {
+    const int e = lane + 64 * p;
+    float z = 0.0f;
+    if (e < N) {
+      z = ws[(long long)t * N + e];
+      for (int s = 1; s < S; ++s) z += ws[((long long)s * T + t) * N + e];
     }
+    scr[p] = e < N ? sigmoidf_acc(z) : 0.0f;
+    key[p] = e < N ? scr[p] + bias[e] : 0.0f;
+    if (scores && e < N) scores[(long long)t * N + e] = scr[p];
   }
-  __syncthreads();
-
-  float b[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int e = lane + 64 * s;
-    b[s] = e < N ? bias[e] : 0.0f;
-  }
-  for (int tl = wave; tl < kBT; tl += 4) {
-    const int t = t0 + tl;
-    if (t >= T) break;
-    float key[4], scr[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int e = lane + 64 * s;
-      scr[s] = e < N ? sc[tl * ldsc + e] : 0.0f;
-      key[s] = scr[s] + b[s];
-    }
-    int sel;
-    float s_sel, sum;
-    wave_topk<4>(key, scr, N, k, lane, sel, s_sel, sum);
-    if (lane < k) {
-      topk_idx[(long long)t * k + lane] = sel;
-      topk_gate[(long long)t * k + lane] = sum > 0.0f ? s_sel / sum : 1.0f / (float)k;
-    }
+  int sel;
+  float s_sel, sum;
+  wave_topk<PER>(key, scr, N, k, lane, sel, s_sel, sum);
+  if (lane < k) {
+    idx[(long long)t * k + lane] = sel;
+    gate[(long long)t * k + lane] = sum > 0.0f ? s_sel / sum : 1.0f / (float)k;
   }
 }
 
@@ -244,31 +292,50 @@ __global__ __launch_bounds__(256) void topk_scores_kernel(const float* __restric
 
 }  // namespace
 
+extern "C" size_t moe_route_workspace_bytes(int T, int H, int N) {
+  if (T <= 0 || H <= 0 || H % 128 != 0 || N <= 0) return 0;
+  return (size_t)route_splits(T, H) * (size_t)T * (size_t)N * sizeof(float);
+}
+
 extern "C" moe_status_t moe_route_topk(const void* x_bf16, const void* w_router_bf16,
                                        const float* bias, int T, int H, int N, int k,
                                        float* scores, int32_t* topk_idx, float* topk_gate,
-                                       hipStream_t stream) {
+                                       void* ws, size_t ws_bytes, hipStream_t stream) {
   if (T < 0 || H < 0 || H % 128 != 0 || N < 16 || N > kMaxN || N % 16 != 0 || k < 1 ||
       k > 32 || k > N)
     return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
   if (H == 0) return MOE_ERR_SHAPE;
+  // in-kernel byte offsets are 32-bit
+  if ((long long)T * H * 2 >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   if (!x_bf16 || !w_router_bf16 || !bias || !topk_idx || !topk_gate) return MOE_ERR_NULL;
-  if (!aligned16(x_bf16) || !aligned16(w_router_bf16)) return MOE_ERR_ALIGN;
-  if (moe_status_t s = check_device()) return s;
-  const size_t lds = 2 * (size_t)(kBT + kMaxN) * 128;   // >= the score tile
+  if (!ws || ws_bytes < moe_route_workspace_bytes(T, H, N)) return MOE_ERR_WORKSPACE;
+  if (!aligned16(x_bf16) || !aligned16(w_router_bf16) || !aligned16(ws)) return MOE_ERR_ALIGN;
+  if (moe_status_t st = check_device()) return st;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_topk_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_partial_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kRLds);
     if (e != hipSuccess) return hip_fail(e);
     attr_set = true;
   }
-  const int blocks = (T + kBT - 1) / kBT;
-  hipLaunchKernelGGL(route_topk_kernel, dim3(blocks), dim3(256), lds, stream,
+  const int S = route_splits(T, H);
+  const int tiles = (T + kRT - 1) / kRT;
+  const int grid = (tiles * S + 7) / 8 * 8;
+  float* part = static_cast<float*>(ws);
+  hipLaunchKernelGGL(route_partial_kernel, dim3(grid), dim3(kRThreads), kRLds, stream,
                      static_cast<const uint16_t*>(x_bf16),
-                     static_cast<const uint16_t*>(w_router_bf16), bias, T, H, N, k, scores,
-                     topk_idx, topk_gate);
+                     static_cast<const uint16_t*>(w_router_bf16), T, H, N, S, part);
+  if (moe_status_t st = launch_status()) return st;
+  const int blocks = (T + 3) / 4;
+  const int per = (N + 63) / 64;
+#define MOE_FINISH_LAUNCH(P)                                                                  \
+  hipLaunchKernelGGL(route_finish_kernel<P>, dim3(blocks), dim3(256), 0, stream, part, S, bias, \
+                     T, N, k, scores, topk_idx, topk_gate)
+  if (per <= 1) MOE_FINISH_LAUNCH(1);
+  else if (per <= 2) MOE_FINISH_LAUNCH(2);
+  else MOE_FINISH_LAUNCH(4);
+#undef MOE_FINISH_LAUNCH
   return launch_status();
 }
 

@@ -70,12 +70,17 @@ typedef enum {
  *   gate[t,j]= s[t,idx[t,j]] / sum_j' s[t,idx[t,j']]  (the bias never enters)
  * x_bf16 [T,H], w_router_bf16 [N,H] (row i is expert i's centroid), bias [N]
  * float.  scores [T,N] float is written when non-NULL.  topk_idx int32 [T,k],
- * topk_gate float [T,k].
- * Requires H % 128 == 0, 1 <= N <= 256, N % 16 == 0, 1 <= k <= min(N, 32).
+ * topk_gate float [T,k].  The sum over h is split into slices whose float
+ * partial sums are added in slice order (deterministic); ws is device scratch
+ * of at least moe_route_workspace_bytes(T, H, N) bytes, 16-byte aligned
+ * (MOE_ERR_WORKSPACE otherwise).
+ * Requires H % 128 == 0, 16 <= N <= 256, N % 16 == 0, 1 <= k <= min(N, 32),
+ * T * H * 2 < 2^31 (MOE_ERR_UNSUPPORTED otherwise).
  */
+size_t moe_route_workspace_bytes(int T, int H, int N);
 moe_status_t moe_route_topk(const void* x_bf16, const void* w_router_bf16, const float* bias,
                             int T, int H, int N, int k, float* scores, int32_t* topk_idx,
-                            float* topk_gate, hipStream_t stream);
+                            float* topk_gate, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * The selection and gate steps alone, from a given float score tensor

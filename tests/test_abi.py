@@ -29,7 +29,7 @@ def lib():
 
 def test_header_declares_the_layer_calls():
     names = declared_functions()
-    for n in ["moe_route_topk", "moe_topk_from_scores", "moe_permute",
+    for n in ["moe_route_topk", "moe_route_workspace_bytes", "moe_topk_from_scores", "moe_permute",
               "moe_permute_workspace_bytes", "fp8_quant_1x128", "fp8_quant_128x128",
               "moe_grouped_gemm_fp8", "moe_combine", "moe_bias_update", "moe_status_str",
               "moe_last_hip_error"]:
@@ -63,10 +63,19 @@ def test_validation_before_any_launch(lib):
     assert lib.fp8_quant_1x128(None, 0, 0, 128, 128, None, None, None) == 0     # empty: no-op
     assert lib.fp8_quant_1x128(None, 0, 4, 128, 128, None, None, None) == 1     # NULL
     assert lib.fp8_quant_1x128(ctypes.c_void_p(8), 0, 4, 128, 128, dummy, dummy, None) == 3
-    lib.moe_route_topk.argtypes = [P, P, P, I, I, I, I, P, P, P, P]
-    assert lib.moe_route_topk(None, None, None, 4, 256, 257, 8, None, None, None, None) == 2
-    assert lib.moe_route_topk(None, None, None, 4, 256, 16, 17, None, None, None, None) == 2
-    assert lib.moe_route_topk(None, None, None, 0, 256, 16, 2, None, None, None, None) == 0
+    lib.moe_route_topk.argtypes = [P, P, P, I, I, I, I, P, P, P, P, ctypes.c_size_t, P]
+    assert lib.moe_route_topk(None, None, None, 4, 256, 257, 8, None, None, None, None, 0, None) == 2
+    assert lib.moe_route_topk(None, None, None, 4, 256, 16, 17, None, None, None, None, 0, None) == 2
+    assert lib.moe_route_topk(None, None, None, 0, 256, 16, 2, None, None, None, None, 0, None) == 0
+    # missing workspace
+    assert lib.moe_route_topk(dummy, dummy, dummy, 4, 256, 16, 2, None, dummy, dummy, None, 0,
+                              None) == 4
+    lib.moe_route_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_route_workspace_bytes.argtypes = [I, I, I]
+    # 8192 tokens of H 7168: 64 token tiles, 4 slices of the 112 chunks
+    assert lib.moe_route_workspace_bytes(8192, 7168, 256) == 4 * 8192 * 256 * 4
+    assert lib.moe_route_workspace_bytes(64, 256, 16) == 4 * 64 * 16 * 4
+    assert lib.moe_route_workspace_bytes(0, 256, 16) == 0
     lib.moe_combine.argtypes = [P, P, P, I, I, I, I, P, P, P]
     assert lib.moe_combine(None, None, None, 0, 4, 12, 2, None, None, None) == 2   # H % 8
     lib.moe_bias_update.argtypes = [P, P, I, I, I, ctypes.c_float, P]

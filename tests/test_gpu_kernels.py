@@ -165,9 +165,14 @@ def test_topk_from_scores_bit_exact(T, N, k, ties):
 
 
 def _route_check(x_bits, wr_bits, b, k, s_gpu, idx_gpu, gate_gpu, delta=3e-5):
-    """Scores within 1e-5 of the float64 oracle; indices bit-exact on every
+    """Indices bit-exact to the selection rule on the GPU's own scores (every
+    token); scores within 1e-5 of the float64 oracle; indices bit-exact on every
     token whose k-th/(k+1)-th key gap exceeds delta (three times the score
     tolerance), a valid top-k of the float64 keys on the others."""
+    # same-score check: on every token the selection is bit-exact to the
+    # oracle's selection rule applied to the GPU's own float32 scores
+    assert np.array_equal(idx_gpu, route.select_topk(s_gpu, b, k))
+    np.testing.assert_allclose(gate_gpu, route.gates(s_gpu, idx_gpu), rtol=2e-6, atol=1e-7)
     s64 = route.router_scores(synth.as_f64(x_bits), synth.as_f64(wr_bits))
     err = np.max(np.abs(s_gpu - s64))
     print(f"max |score - oracle| = {err:.3e}")
@@ -207,10 +212,12 @@ def test_route_topk(name, T):
 
 
 def test_route_topk_ragged_small():
-    """T not a multiple of the 32-token tile, N = k (all chosen), N = 16."""
+    """T not a multiple of the 128-token tile, N = k (all chosen), N = 16, N
+    not a multiple of 64 (partly empty expert bands), H of one 128 block."""
     moe = _moe()
     rng = np.random.default_rng(5)
-    for T, H, N, k in [(33, 128, 16, 16), (70, 384, 32, 3), (1, 256, 16, 1)]:
+    for T, H, N, k in [(33, 128, 16, 16), (70, 384, 32, 3), (1, 256, 16, 1), (129, 640, 80, 6),
+                       (300, 1024, 208, 8)]:
         x = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
         wr = synth.f32_to_bf16_bits((rng.standard_normal((N, H)) * 0.05).astype(np.float32))
         b = rng.uniform(-0.1, 0.1, N).astype(np.float32)
@@ -218,6 +225,25 @@ def test_route_topk_ragged_small():
         idx, gate, s = moe.moe_route_topk(bf16_to_dev(x), bf16_to_dev(wr), to_dev(b), k)
         torch.cuda.synchronize()
         _route_check(x, wr, b, k, s.cpu().numpy(), idx.cpu().numpy(), gate.cpu().numpy())
+
+
+def test_route_topk_full_routing_workload_sampled():
+    """The routing workload at its full size (T = 16384, H 7168, 256 experts,
+    top-8), in the launch configuration the layer uses; the oracle recomputes
+    a seeded sample of 384 tokens (first, last and random rows)."""
+    moe = _moe()
+    w = synth.WORKLOADS["routing"]
+    x = device_tensor(w.x_spec(), w.seed)
+    wrb = w.router_weight()
+    b = w.bias()
+    log(f"moe_route_topk routing full T={w.T}")
+    idx, gate, s = moe.moe_route_topk(x, bf16_to_dev(wrb), to_dev(b), w.k)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, 1, w.T - 1], rng.choice(w.T, 381, replace=False)]))
+    xb = synth.generate(w.x_spec(), w.seed, rows=rows)
+    _route_check(xb, wrb, b, w.k, s.cpu().numpy()[rows], idx.cpu().numpy()[rows],
+                 gate.cpu().numpy()[rows])
 
 
 # --------------------------------------------------------------------------- permutation
