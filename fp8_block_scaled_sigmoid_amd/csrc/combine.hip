@@ -23,9 +23,14 @@ __global__ __launch_bounds__(kCombineBlock) void combine_kernel(
     const uint16_t* __restrict__ out, const float* __restrict__ gate,
     const int32_t* __restrict__ row_of, int shared_row0, int T, int H, int k,
     const uint16_t* __restrict__ residual, uint16_t* __restrict__ y) {
-  const int c8 = blockIdx.x * kCombineBlock + threadIdx.x;  // 8-column chunk
-  if (c8 * 8 >= H) return;
-  for (int t = blockIdx.y; t < T; t += gridDim.y) {
+  // one work item = one token x one 8-column chunk, flattened so every lane
+  // of every block has work whatever H is
+  const int chunks = H >> 3;
+  const long long items = (long long)T * chunks;
+  for (long long item = (long long)blockIdx.x * kCombineBlock + threadIdx.x; item < items;
+       item += (long long)gridDim.x * kCombineBlock) {
+    const int t = (int)(item / chunks);
+    const int c8 = (int)(item - (long long)t * chunks);
     float acc[8];
     const long long col = (long long)c8 * 8;
     uint4 base = make_uint4(0, 0, 0, 0);
@@ -103,9 +108,10 @@ extern "C" moe_status_t moe_combine(const void* out_rows_bf16, const float* gate
       (residual_bf16 && !aligned16(residual_bf16)))
     return MOE_ERR_ALIGN;
   if (moe_status_t s = check_device()) return s;
-  const int cblocks = (H / 8 + kCombineBlock - 1) / kCombineBlock;
-  const int ty = T < 65535 ? T : 65535;
-  hipLaunchKernelGGL(combine_kernel, dim3(cblocks, ty), dim3(kCombineBlock), 0, stream,
+  const long long items = (long long)T * (H / 8);
+  long long blocks = (items + kCombineBlock - 1) / kCombineBlock;
+  if (blocks > (1LL << 20)) blocks = 1LL << 20;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(kCombineBlock), 0, stream,
                      static_cast<const uint16_t*>(out_rows_bf16), gate, row_of, shared_row0, T, H,
                      k, static_cast<const uint16_t*>(residual_bf16), static_cast<uint16_t*>(y_bf16));
   return launch_status();

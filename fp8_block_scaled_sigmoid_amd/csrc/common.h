@@ -14,23 +14,22 @@ namespace moe {
 
 // ---------------------------------------------------------------------------
 // E4M3 ("fn", max 448) encoder: round to nearest, ties to the even code,
-// saturating, sign kept.  Written from the format's definition: three mantissa
-// bits on a grid of step 2^(e-3) for normal magnitudes 2^-6 <= |v| < 448, and
-// a fixed step of 2^-9 below 2^-6.
+// saturating, sign kept.  gfx950's float -> OCP E4M3 conversion rounds to
+// nearest even and keeps the sign; clamping to +-448 first gives the
+// saturation (without it, magnitudes of 464 and above would become NaN).  This
+// equals the format's definition on every finite float (checked exhaustively
+// against a step-by-step software encoder on the device).
+__device__ __forceinline__ float e4m3_clamp(float v) {
+  return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+}
 __device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a >= 0x43E00000u) {            // |v| >= 448: saturate
-    code = 0x7Eu;
-  } else if (a < 0x3C800000u) {      // |v| < 2^-6: multiples of 2^-9 (0..8)
-    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  } else {                           // keep 3 of the 23 mantissa bits, RNE
-    const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
-    code = r - (120u << 3);          // exponent bias 127 -> 7
-  }
-  return code | sign;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(v), 0.0f, 0, false) & 0xFFu;
+}
+// four codes packed little-endian: a in bits 0-7, b 8-15, c 16-23, d 24-31
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), w, true);
+  return (uint32_t)w;
 }
 
 // float -> bf16 bits, round to nearest even (inputs are finite).

@@ -33,16 +33,17 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// codes of v * m, or all zero when m == 0 (the zero-tile rule: no -0 codes)
 __device__ __forceinline__ uint2 encode8(const float (&v)[8], float m) {
   uint2 o;
-  o.x = quant_code(v[0], m) | (quant_code(v[1], m) << 8) | (quant_code(v[2], m) << 16) |
-        (quant_code(v[3], m) << 24);
-  o.y = quant_code(v[4], m) | (quant_code(v[5], m) << 8) | (quant_code(v[6], m) << 16) |
-        (quant_code(v[7], m) << 24);
+  o.x = e4m3_pack4(v[0] * m, v[1] * m, v[2] * m, v[3] * m);
+  o.y = e4m3_pack4(v[4] * m, v[5] * m, v[6] * m, v[7] * m);
+  if (m == 0.0f) o = make_uint2(0u, 0u);
   return o;
 }
 
-// x [rows, ld] -> q [rows, cols], d [rows, cols/128]
+// x [rows, ld] -> q [rows, cols], d [rows, cols/128].  Each 16-lane group
+// takes two tiles per pass (both loads issued before either is used).
 template <typename InT>
 __global__ __launch_bounds__(kQuantBlock) void quant_1x128_kernel(
     const InT* __restrict__ x, int rows, int cols, int ld, uint8_t* __restrict__ q,
@@ -50,26 +51,36 @@ __global__ __launch_bounds__(kQuantBlock) void quant_1x128_kernel(
   const int tiles_per_row = cols >> 7;
   const long long n_tiles = (long long)rows * tiles_per_row;
   const int sub = threadIdx.x & 15;
+  const long long groups = (long long)gridDim.x * (kQuantBlock / 16);
   for (long long tile = (long long)blockIdx.x * (kQuantBlock / 16) + (threadIdx.x >> 4);
-       tile - (threadIdx.x >> 4) < n_tiles; tile += (long long)gridDim.x * (kQuantBlock / 16)) {
-    const bool live = tile < n_tiles;
-    float v[8];
-    float amax = 0.0f;
-    long long r = 0;
-    int j = 0;
-    if (live) {
-      r = tile / tiles_per_row;
-      j = (int)(tile - r * tiles_per_row);
-      load8<InT>(x + r * (long long)ld + j * 128 + sub * 8, v);
+       tile - (threadIdx.x >> 4) < n_tiles; tile += 2 * groups) {
+    float v[2][8];
+    float amax[2] = {0.0f, 0.0f};
+    long long r[2];
+    int j[2];
+    bool live[2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    for (int u = 0; u < 2; ++u) {
+      const long long t = tile + u * groups;
+      live[u] = t < n_tiles;
+      r[u] = live[u] ? t / tiles_per_row : 0;
+      j[u] = live[u] ? (int)(t - r[u] * tiles_per_row) : 0;
+      if (live[u]) load8<InT>(x + r[u] * (long long)ld + j[u] * 128 + sub * 8, v[u]);
     }
-    amax = group_max<16>(amax);
-    if (live) {
-      float m, dd;
-      tile_scale(amax, m, dd);
-      *reinterpret_cast<uint2*>(q + r * (long long)cols + j * 128 + sub * 8) = encode8(v, m);
-      if (sub == 0) d[r * tiles_per_row + j] = dd;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (live[u]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax[u] = fmaxf(amax[u], fabsf(v[u][i]));
+      }
+      amax[u] = group_max<16>(amax[u]);
+      if (live[u]) {
+        float m, dd;
+        tile_scale(amax[u], m, dd);
+        *reinterpret_cast<uint2*>(q + r[u] * (long long)cols + j[u] * 128 + sub * 8) =
+            encode8(v[u], m);
+        if (sub == 0) d[r[u] * tiles_per_row + j[u]] = dd;
+      }
     }
   }
 }
@@ -119,7 +130,7 @@ extern "C" moe_status_t fp8_quant_1x128(const void* x, moe_dtype_t dt, int rows,
   if (!aligned16(x) || !aligned16(q) || (reinterpret_cast<uintptr_t>(d) & 3)) return MOE_ERR_ALIGN;
   if (moe_status_t s = check_device()) return s;
   const long long tiles = (long long)rows * (cols / 128);
-  long long blocks = (tiles + 15) / 16;
+  long long blocks = (tiles + 31) / 32;   // 16 groups of 16 lanes, two tiles each
   if (blocks > 65536) blocks = 65536;
   if (dt == MOE_BF16)
     hipLaunchKernelGGL(quant_1x128_kernel<uint16_t>, dim3((unsigned)blocks), dim3(kQuantBlock), 0,
