@@ -308,16 +308,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
         const i32x4 y1 = *reinterpret_cast<const i32x4*>(b_hi + ni * 16 * 128);
         return __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
       };
+      // read order = use order: A0 and B0 first, so the first MFMA waits for
+      // four reads only, then the other A fragments, then the row scales
+      // (first needed by the FMAs behind the second column subtile)
       f32x4 sc[4];
       i32x8 af[4], bfr[2];
-#pragma unroll
-      for (int mi = 0; mi < NMI; ++mi) {
+      auto read_a = [&](int mi) {
         const i32x4 x0 = *reinterpret_cast<const i32x4*>(a_lo + mi * 16 * 128);
         const i32x4 x1 = *reinterpret_cast<const i32x4*>(a_hi + mi * 16 * 128);
-        af[mi] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-        sc[mi] = *reinterpret_cast<const f32x4*>(sA + mi * 16);
-      }
+        return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      af[0] = read_a(0);
       bfr[0] = read_b(0);
+#pragma unroll
+      for (int mi = 1; mi < NMI; ++mi) af[mi] = read_a(mi);
+#pragma unroll
+      for (int mi = 0; mi < NMI; ++mi) sc[mi] = *reinterpret_cast<const f32x4*>(sA + mi * 16);
 #pragma unroll
       for (int mi = 0; mi < NMI; ++mi) sc[mi] = sc[mi] * sb;
       f32x4 part[2][4];
