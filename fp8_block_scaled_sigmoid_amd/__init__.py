@@ -55,8 +55,8 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build()")
         L = ctypes.CDLL(LIB_PATH)
         sig = {
-            "moe_route_topk": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, ctypes.c_size_t, _P],
-            "moe_topk_from_scores": [_P, _P, _I, _I, _I, _P, _P, _P],
+            "moe_route_topk": [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, ctypes.c_size_t, _P],
+            "moe_topk_from_scores": [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P],
             "moe_permute": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
             "fp8_quant_1x128": [_P, _I, _I, _I, _I, _P, _P, _P],
             "fp8_quant_128x128": [_P, _I, _I, _I, _I, _P, _P, _P],
@@ -110,11 +110,13 @@ def moe_route_workspace_bytes(T, H, N):
     return int(lib().moe_route_workspace_bytes(T, H, N))
 
 
-def moe_route_topk(x, w_router, bias, k, scores=True, idx=None, gate=None, ws=None, stream=None):
+def moe_route_topk(x, w_router, bias, k, scores=True, idx=None, gate=None, ws=None,
+                   n_groups=1, topk_groups=1, stream=None):
     """Sigmoid router + biased top-k.  x [T,H] bf16, w_router [N,H] bf16,
     bias [N] float32.  Returns (idx int32 [T,k], gate float32 [T,k],
     scores float32 [T,N] or None).  ws: optional uint8 device scratch of
-    moe_route_workspace_bytes(T, H, N) bytes."""
+    moe_route_workspace_bytes(T, H, N) bytes.  n_groups > 1 turns on the
+    group-limited selection (the best topk_groups groups are eligible)."""
     T, H = x.shape
     N = w_router.shape[0]
     _dev(x, torch.bfloat16, "x"), _dev(w_router, torch.bfloat16, "w_router")
@@ -129,18 +131,20 @@ def moe_route_topk(x, w_router, bias, k, scores=True, idx=None, gate=None, ws=No
         ws = torch.empty(max(moe_route_workspace_bytes(T, H, N), 16), dtype=torch.uint8,
                          device=x.device)
     _check("moe_route_topk", lib().moe_route_topk(_ptr(x), _ptr(w_router), _ptr(bias), T, H, N, k,
-                                                  _ptr(scores), _ptr(idx), _ptr(gate), _ptr(ws),
-                                                  ws.numel(), _stream(stream)))
+                                                  n_groups, topk_groups, _ptr(scores), _ptr(idx),
+                                                  _ptr(gate), _ptr(ws), ws.numel(), _stream(stream)))
     return idx, gate, scores
 
 
-def moe_topk_from_scores(scores, bias, k, idx=None, gate=None, stream=None):
+def moe_topk_from_scores(scores, bias, k, idx=None, gate=None, n_groups=1, topk_groups=1,
+                         stream=None):
     T, N = scores.shape
     _dev(scores, torch.float32, "scores"), _dev(bias, torch.float32, "bias")
     idx = torch.empty(T, k, dtype=torch.int32, device=scores.device) if idx is None else idx
     gate = torch.empty(T, k, dtype=torch.float32, device=scores.device) if gate is None else gate
     _check("moe_topk_from_scores", lib().moe_topk_from_scores(
-        _ptr(scores), _ptr(bias), T, N, k, _ptr(idx), _ptr(gate), _stream(stream)))
+        _ptr(scores), _ptr(bias), T, N, k, n_groups, topk_groups, _ptr(idx), _ptr(gate),
+        _stream(stream)))
     return idx, gate
 
 
@@ -265,9 +269,10 @@ class MoELayer:
     """Buffers for a batch of T tokens and the forward pass over them.  All
     buffers are allocated once here; ``forward`` only enqueues kernels."""
 
-    def __init__(self, weights, T, k, gamma=1e-3, device="cuda"):
+    def __init__(self, weights, T, k, gamma=1e-3, device="cuda", n_groups=1, topk_groups=1):
         w = weights
         self.w, self.T, self.k, self.gamma = w, T, k, gamma
+        self.n_groups, self.topk_groups = n_groups, topk_groups
         N, H, I = w.N, w.H, w.I
         self.with_shared = w.G == N + 1
         R = T * k + (T if self.with_shared else 0)
@@ -293,7 +298,8 @@ class MoELayer:
     # the individual steps, so that callers can time or replace one of them
     def route(self, x, stream=None):
         moe_route_topk(x, self.w.w_router, self.w.bias, self.k, scores=self.scores, idx=self.idx,
-                       gate=self.gate, ws=self.route_ws, stream=stream)
+                       gate=self.gate, ws=self.route_ws, n_groups=self.n_groups,
+                       topk_groups=self.topk_groups, stream=stream)
 
     def permute(self, stream=None):
         moe_permute(self.idx, self.w.N, self.with_shared,

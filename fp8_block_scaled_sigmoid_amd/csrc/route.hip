@@ -58,8 +58,8 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 template <int PER>
 __device__ __forceinline__ void wave_topk(const float (&key)[PER], const float (&score)[PER],
                                           int N, int k, int lane, int& sel_idx, float& sel_s,
-                                          float& sum) {
-  uint32_t taken = 0;
+                                          float& sum, uint32_t excluded = 0u) {
+  uint32_t taken = excluded;
   sum = 0.0f;
   sel_idx = -1;
   sel_s = 0.0f;
@@ -89,6 +89,61 @@ __device__ __forceinline__ void wave_topk(const float (&key)[PER], const float (
       sel_s = s_e;
     }
   }
+}
+
+__device__ __forceinline__ float unsortable(uint32_t v) {
+  return __uint_as_float((v & 0x80000000u) ? (v & 0x7FFFFFFFu) : ~v);
+}
+
+// Group-limited routing ("DeepSeek-V3, explained.", recipe step 5; "DeepSeek-V3
+// Technical Report" (deepforge), "Balancing without a balance loss"): the N
+// experts form G groups of N / G consecutive indices; a group's score is the
+// float sum of its r largest keys, added in descending order; only the M best
+// groups (score descending, group index ascending) are eligible.  Returns the
+// slots of this lane (expert lane + 64 p) that are NOT eligible, as a bit
+// mask.  Requires G <= 64.
+template <int PER>
+__device__ __forceinline__ uint32_t group_excluded(const float (&key)[PER], int N, int G, int M,
+                                                   int r, int lane) {
+  const int gs = N / G;
+  float my_score = 0.0f;                    // lane g < G: score of group g
+  for (int g = 0; g < G; ++g) {
+    uint32_t taken = 0;
+    float acc = 0.0f;
+    for (int j = 0; j < r; ++j) {
+      unsigned long long best = 0ull;
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int e = lane + 64 * p;
+        if (e < N && e / gs == g && !((taken >> p) & 1u)) {
+          const unsigned long long c =
+              ((unsigned long long)sortable(key[p]) << 32) | (0xFFFFFFFFu - (uint32_t)e);
+          best = c > best ? c : best;
+        }
+      }
+      best = wave_max_u64(best);
+      const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+      if (lane == (e & 63)) taken |= 1u << (e >> 6);
+      const float kv = unsortable((uint32_t)(best >> 32));
+      acc = j == 0 ? kv : acc + kv;
+    }
+    if (lane == g) my_score = acc;
+  }
+  int rank = 0;
+  for (int g = 0; g < G; ++g) {
+    const float sg = __shfl(my_score, g, 64);
+    if (sg > my_score || (sg == my_score && g < lane)) ++rank;
+  }
+  const int chosen = (lane < G && rank < M) ? 1 : 0;
+  uint32_t excluded = 0;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int e = lane + 64 * p;
+    const int g = e < N ? e / gs : 0;
+    const int ok = __shfl(chosen, g, 64);
+    if (e >= N || !ok) excluded |= 1u << p;
+  }
+  return excluded;
 }
 
 __device__ __forceinline__ float sigmoidf_acc(float z) { return 1.0f / (1.0f + expf(-z)); }
@@ -237,7 +292,8 @@ __global__ __launch_bounds__(kRThreads, 1) void route_partial_kernel(
 template <int PER>
 __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restrict__ ws, int S,
                                                            const float* __restrict__ bias, int T,
-                                                           int N, int k, float* __restrict__ scores,
+                                                           int N, int k, int G, int M,
+                                                           float* __restrict__ scores,
                                                            int32_t* __restrict__ idx,
                                                            float* __restrict__ gate) {
   const int lane = threadIdx.x & 63;
@@ -256,9 +312,10 @@ __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restri
     key[p] = e < N ? scr[p] + bias[e] : 0.0f;
     if (scores && e < N) scores[(long long)t * N + e] = scr[p];
   }
+  const uint32_t excluded = G > 1 ? group_excluded<PER>(key, N, G, M, k / M, lane) : 0u;
   int sel;
   float s_sel, sum;
-  wave_topk<PER>(key, scr, N, k, lane, sel, s_sel, sum);
+  wave_topk<PER>(key, scr, N, k, lane, sel, s_sel, sum, excluded);
   if (lane < k) {
     idx[(long long)t * k + lane] = sel;
     gate[(long long)t * k + lane] = sum > 0.0f ? s_sel / sum : 1.0f / (float)k;
@@ -269,7 +326,8 @@ __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restri
 template <int PER>
 __global__ __launch_bounds__(256) void topk_scores_kernel(const float* __restrict__ scores,
                                                           const float* __restrict__ bias, int T,
-                                                          int N, int k, int32_t* __restrict__ idx,
+                                                          int N, int k, int G, int M,
+                                                          int32_t* __restrict__ idx,
                                                           float* __restrict__ gate) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -281,13 +339,22 @@ __global__ __launch_bounds__(256) void topk_scores_kernel(const float* __restric
     scr[s] = e < N ? scores[(long long)t * N + e] : 0.0f;
     key[s] = e < N ? scr[s] + bias[e] : 0.0f;
   }
+  const uint32_t excluded = G > 1 ? group_excluded<PER>(key, N, G, M, k / M, lane) : 0u;
   int sel;
   float s_sel, sum;
-  wave_topk<PER>(key, scr, N, k, lane, sel, s_sel, sum);
+  wave_topk<PER>(key, scr, N, k, lane, sel, s_sel, sum, excluded);
   if (lane < k) {
     idx[(long long)t * k + lane] = sel;
     gate[(long long)t * k + lane] = sum > 0.0f ? s_sel / sum : 1.0f / (float)k;
   }
+}
+
+// group-limited routing arguments: G <= 1 disables it; otherwise G divides N,
+// 1 <= M <= G, M divides k and each group holds at least k / M experts
+bool groups_ok(int N, int k, int G, int M) {
+  if (G <= 1) return true;
+  if (G > 64 || N % G != 0 || M < 1 || M > G || k % M != 0) return false;
+  return k / M <= N / G && k <= M * (N / G);
 }
 
 }  // namespace
@@ -299,10 +366,11 @@ extern "C" size_t moe_route_workspace_bytes(int T, int H, int N) {
 
 extern "C" moe_status_t moe_route_topk(const void* x_bf16, const void* w_router_bf16,
                                        const float* bias, int T, int H, int N, int k,
-                                       float* scores, int32_t* topk_idx, float* topk_gate,
-                                       void* ws, size_t ws_bytes, hipStream_t stream) {
+                                       int n_groups, int topk_groups, float* scores,
+                                       int32_t* topk_idx, float* topk_gate, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
   if (T < 0 || H < 0 || H % 128 != 0 || N < 16 || N > kMaxN || N % 16 != 0 || k < 1 ||
-      k > 32 || k > N)
+      k > 32 || k > N || !groups_ok(N, k, n_groups, topk_groups))
     return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
   if (H == 0) return MOE_ERR_SHAPE;
@@ -331,7 +399,7 @@ extern "C" moe_status_t moe_route_topk(const void* x_bf16, const void* w_router_
   const int per = (N + 63) / 64;
 #define MOE_FINISH_LAUNCH(P)                                                                  \
   hipLaunchKernelGGL(route_finish_kernel<P>, dim3(blocks), dim3(256), 0, stream, part, S, bias, \
-                     T, N, k, scores, topk_idx, topk_gate)
+                     T, N, k, n_groups, topk_groups, scores, topk_idx, topk_gate)
   if (per <= 1) MOE_FINISH_LAUNCH(1);
   else if (per <= 2) MOE_FINISH_LAUNCH(2);
   else MOE_FINISH_LAUNCH(4);
@@ -340,9 +408,12 @@ extern "C" moe_status_t moe_route_topk(const void* x_bf16, const void* w_router_
 }
 
 extern "C" moe_status_t moe_topk_from_scores(const float* scores, const float* bias, int T, int N,
-                                             int k, int32_t* topk_idx, float* topk_gate,
+                                             int k, int n_groups, int topk_groups,
+                                             int32_t* topk_idx, float* topk_gate,
                                              hipStream_t stream) {
-  if (T < 0 || N < 1 || N > 1024 || k < 1 || k > 32 || k > N) return MOE_ERR_SHAPE;
+  if (T < 0 || N < 1 || N > 1024 || k < 1 || k > 32 || k > N ||
+      !groups_ok(N, k, n_groups, topk_groups))
+    return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
   if (!scores || !bias || !topk_idx || !topk_gate) return MOE_ERR_NULL;
   if (moe_status_t s = check_device()) return s;
@@ -350,7 +421,7 @@ extern "C" moe_status_t moe_topk_from_scores(const float* scores, const float* b
   const int per = (N + 63) / 64;
 #define MOE_TOPK_LAUNCH(P)                                                                      \
   hipLaunchKernelGGL(topk_scores_kernel<P>, dim3(blocks), dim3(256), 0, stream, scores, bias, T, \
-                     N, k, topk_idx, topk_gate)
+                     N, k, n_groups, topk_groups, topk_idx, topk_gate)
   if (per <= 1) MOE_TOPK_LAUNCH(1);
   else if (per <= 2) MOE_TOPK_LAUNCH(2);
   else if (per <= 4) MOE_TOPK_LAUNCH(4);

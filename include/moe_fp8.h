@@ -68,6 +68,16 @@ typedef enum {
  *   chosen   = the k experts with the largest fl32(s[t,i] + bias[i]),
  *              ties to the lower expert index, listed in that order
  *   gate[t,j]= s[t,idx[t,j]] / sum_j' s[t,idx[t,j']]  (the bias never enters)
+ * Group-limited selection ([VE] recipe step 5; [DF] "Balancing without a
+ * balance loss"; [TP] section V "Custom all-to-all kernels"), on when
+ * n_groups > 1: the N experts form n_groups groups of N / n_groups
+ * consecutive indices (one per node); a group's score is the float32 sum of
+ * its k / topk_groups largest biased keys, added in descending order; only the
+ * topk_groups best groups (score descending, group index ascending) are
+ * eligible, and the k experts are the best keys among them.  n_groups <= 1
+ * turns it off.  Otherwise requires n_groups <= 64, N % n_groups == 0,
+ * 1 <= topk_groups <= n_groups, k % topk_groups == 0 and
+ * k / topk_groups <= N / n_groups (MOE_ERR_SHAPE).
  * x_bf16 [T,H], w_router_bf16 [N,H] (row i is expert i's centroid), bias [N]
  * float.  scores [T,N] float is written when non-NULL.  topk_idx int32 [T,k],
  * topk_gate float [T,k].  The sum over h is split into slices whose float
@@ -79,16 +89,18 @@ typedef enum {
  */
 size_t moe_route_workspace_bytes(int T, int H, int N);
 moe_status_t moe_route_topk(const void* x_bf16, const void* w_router_bf16, const float* bias,
-                            int T, int H, int N, int k, float* scores, int32_t* topk_idx,
-                            float* topk_gate, void* ws, size_t ws_bytes, hipStream_t stream);
+                            int T, int H, int N, int k, int n_groups, int topk_groups,
+                            float* scores, int32_t* topk_idx, float* topk_gate, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
 
 /*
  * The selection and gate steps alone, from a given float score tensor
- * scores [T,N] (same definitions as moe_route_topk).  Requires 1 <= N <= 1024,
- * 1 <= k <= min(N, 32).
+ * scores [T,N] (same definitions as moe_route_topk, group-limited selection
+ * included).  Requires 1 <= N <= 1024, 1 <= k <= min(N, 32).
  */
 moe_status_t moe_topk_from_scores(const float* scores, const float* bias, int T, int N, int k,
-                                  int32_t* topk_idx, float* topk_gate, hipStream_t stream);
+                                  int n_groups, int topk_groups, int32_t* topk_idx,
+                                  float* topk_gate, hipStream_t stream);
 
 /*
  * Per-expert token counts and the token permutation.  Every (token, slot)

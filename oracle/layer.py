@@ -35,16 +35,21 @@ def expert_rows(xq, xd, tokens, wq, g, precision="D"):
                            wq["w2q"][g], wq["w2d"][g], precision)
 
 
-def moe_layer(x, w_r, bias, w1, w2, k, gamma, precision="D", idx=None, wq=None):
+def moe_layer(x, w_r, bias, w1, w2, k, gamma, precision="D", idx=None, wq=None, n_groups=1,
+              topk_groups=1):
     """x [T, H], w_r [N, H], bias [N] float32, w1 [N+1, 2I, H],
     w2 [N+1, H, I] (expert N is the shared one).  ``idx`` overrides the
     oracle's own routing (to line it up with a routing decided elsewhere);
-    ``wq`` supplies already-quantised weights.  Returns a dict of every
-    intermediate."""
+    ``wq`` supplies already-quantised weights; n_groups > 1 selects with the
+    group-limited rule (``route.select_topk_grouped``).  Returns a dict of
+    every intermediate."""
     x = np.asarray(x, np.float64)
     T, H = x.shape
     N = w_r.shape[0]
     s64, s32, idx_o, gate_o = _route.route(x, w_r, bias, k)
+    if n_groups > 1:
+        idx_o = _route.select_topk_grouped(s32, bias, k, n_groups, topk_groups)
+        gate_o = _route.gates(s32, idx_o)
     if idx is None:
         idx = idx_o
         gate = gate_o

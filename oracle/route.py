@@ -17,6 +17,18 @@ Readings where the pages leave a step open:
   * ties are broken by the lower expert index, and the k chosen experts are
     listed in (key descending, index ascending) order;
   * gates are computed in float64 from the float32 scores.
+
+Group-limited selection ([VE] recipe step 5; [DF] "Balancing without a balance
+loss", last sentences; [TP] section V, "Custom all-to-all kernels"): the N
+experts are split into G equal groups of consecutive indices (one group per
+node); a group's score is the sum of its K_r / M highest keys; only the M best
+groups are eligible, and the K_r experts are the best keys among them.
+Readings where the pages leave a step open:
+  * the keys are the biased keys (selection, including the group ranking, is
+    where the bias acts; the gates stay unbiased);
+  * the group score is a float32 sum of the group's K_r / M highest keys taken
+    in descending order, and K_r must be a multiple of M;
+  * groups are ranked by (score descending, group index ascending).
 """
 import numpy as np
 
@@ -54,6 +66,40 @@ def select_topk(s32, bias, k):
     (key descending, index ascending)."""
     key = biased_keys(s32, bias)
     order = np.argsort(-key, axis=1, kind="stable")   # stable: index asc on ties
+    return order[:, :k].astype(np.int32)
+
+
+def group_scores(key, n_groups, per_group):
+    """Float32 score of every group: the sum of its `per_group` largest keys,
+    added in descending order.  key [T, N] float32 -> [T, G] float32."""
+    key = np.asarray(key, np.float32)
+    T, N = key.shape
+    gs = N // n_groups
+    top = -np.sort(-key.reshape(T, n_groups, gs), axis=2)[:, :, :per_group]
+    acc = top[:, :, 0].astype(np.float32)
+    for j in range(1, per_group):
+        acc = (acc.astype(np.float64) + top[:, :, j].astype(np.float64)).astype(np.float32)
+    return acc
+
+
+def select_topk_grouped(s32, bias, k, n_groups, topk_groups):
+    """Group-limited selection: indices [T, k] int32 of the k largest biased
+    keys among the experts of the `topk_groups` best groups (groups ranked by
+    the float32 sum of their k / topk_groups largest keys, ties to the lower
+    group), ordered by (key descending, index ascending)."""
+    key = biased_keys(s32, bias)
+    T, N = key.shape
+    if n_groups <= 1 or topk_groups >= n_groups:
+        return select_topk(s32, bias, k)
+    assert N % n_groups == 0 and k % topk_groups == 0
+    gs = N // n_groups
+    gsc = group_scores(key, n_groups, k // topk_groups)
+    gorder = np.argsort(-gsc, axis=1, kind="stable")[:, :topk_groups]
+    allowed = np.zeros((T, n_groups), dtype=bool)
+    np.put_along_axis(allowed, gorder, True, axis=1)
+    allowed = np.repeat(allowed, gs, axis=1)
+    order = np.lexsort((np.broadcast_to(np.arange(N), key.shape), -key.astype(np.float64),
+                        ~allowed), axis=1)
     return order[:, :k].astype(np.int32)
 
 

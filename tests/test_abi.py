@@ -63,13 +63,25 @@ def test_validation_before_any_launch(lib):
     assert lib.fp8_quant_1x128(None, 0, 0, 128, 128, None, None, None) == 0     # empty: no-op
     assert lib.fp8_quant_1x128(None, 0, 4, 128, 128, None, None, None) == 1     # NULL
     assert lib.fp8_quant_1x128(ctypes.c_void_p(8), 0, 4, 128, 128, dummy, dummy, None) == 3
-    lib.moe_route_topk.argtypes = [P, P, P, I, I, I, I, P, P, P, P, ctypes.c_size_t, P]
-    assert lib.moe_route_topk(None, None, None, 4, 256, 257, 8, None, None, None, None, 0, None) == 2
-    assert lib.moe_route_topk(None, None, None, 4, 256, 16, 17, None, None, None, None, 0, None) == 2
-    assert lib.moe_route_topk(None, None, None, 0, 256, 16, 2, None, None, None, None, 0, None) == 0
-    # missing workspace
-    assert lib.moe_route_topk(dummy, dummy, dummy, 4, 256, 16, 2, None, dummy, dummy, None, 0,
-                              None) == 4
+    lib.moe_route_topk.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P, ctypes.c_size_t, P]
+    R = lambda T, H, N, k, G=1, M=1, x=None, ws=None: lib.moe_route_topk(  # noqa: E731
+        x, x, x, T, H, N, k, G, M, None, x, x, ws, 0, None)
+    assert R(4, 256, 257, 8) == 2
+    assert R(4, 256, 16, 17) == 2
+    assert R(0, 256, 16, 2) == 0
+    # group-limited arguments: G must divide N, M <= G, M | k, k / M <= N / G
+    assert R(4, 256, 256, 8, 3, 1) == 2
+    assert R(4, 256, 256, 8, 8, 9) == 2
+    assert R(4, 256, 256, 8, 8, 3) == 2
+    assert R(4, 256, 16, 8, 8, 2) == 2            # 4 per group > 2 experts per group
+    assert R(4, 256, 256, 8, 128, 4) == 2         # more than 64 groups
+    assert R(0, 256, 256, 8, 8, 4) == 0
+    # missing workspace (checked before any device access)
+    assert R(4, 256, 16, 2, x=dummy) == 4
+    assert R(4, 256, 256, 8, 8, 4, x=dummy) == 4
+    lib.moe_topk_from_scores.argtypes = [P, P, I, I, I, I, I, P, P, P]
+    assert lib.moe_topk_from_scores(None, None, 4, 256, 8, 8, 3, None, None, None) == 2
+    assert lib.moe_topk_from_scores(None, None, 0, 256, 8, 8, 4, None, None, None) == 0
     lib.moe_route_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_route_workspace_bytes.argtypes = [I, I, I]
     # 8192 tokens of H 7168: 64 token tiles, 4 slices of the 112 chunks

@@ -246,6 +246,52 @@ def test_route_topk_full_routing_workload_sampled():
                  gate.cpu().numpy()[rows])
 
 
+@pytest.mark.parametrize("T,N,G,M,k,ties", [(1000, 256, 8, 4, 8, False), (777, 256, 8, 4, 8, True),
+                                            (300, 64, 4, 2, 4, False), (200, 960, 60, 6, 12, True),
+                                            (64, 16, 2, 1, 2, False), (50, 48, 3, 3, 3, True)])
+def test_topk_from_scores_grouped_bit_exact(T, N, G, M, k, ties):
+    """Group-limited selection against the oracle's, bit-exact, with and
+    without exact ties in the scores (group ties included)."""
+    moe = _moe()
+    rng = np.random.default_rng(T + N + G)
+    s = rng.uniform(0, 1, (T, N)).astype(np.float32)
+    b = rng.uniform(-0.05, 0.05, N).astype(np.float32)
+    if ties:
+        s = (np.round(s * 8) / 8).astype(np.float32)
+        b[:] = 0
+    log(f"moe_topk_from_scores grouped T={T} N={N} G={G} M={M} k={k}")
+    idx, gate = moe.moe_topk_from_scores(to_dev(s), to_dev(b), k, n_groups=G, topk_groups=M)
+    torch.cuda.synchronize()
+    want = route.select_topk_grouped(s, b, k, G, M)
+    assert np.array_equal(idx.cpu().numpy(), want)
+    np.testing.assert_allclose(gate.cpu().numpy(), route.gates(s, want), rtol=2e-6, atol=1e-7)
+
+
+def test_route_topk_grouped_v3_shape():
+    """The fused router with 8 groups of 32 experts, 4 groups eligible, at the
+    DeepSeek-V3 shape: bit-exact to the oracle's group-limited rule on the
+    GPU's own scores, every token within 4 groups, and different from the
+    plain top-k on some tokens."""
+    moe = _moe()
+    w = synth.WORKLOADS["prefill"]
+    T = 2048
+    xb = synth.generate(w.x_spec(), w.seed, rows=np.arange(T))
+    wrb = w.router_weight()
+    b = w.bias()
+    log(f"moe_route_topk grouped T={T}")
+    idx, gate, s = moe.moe_route_topk(bf16_to_dev(xb), bf16_to_dev(wrb), to_dev(b), w.k,
+                                      n_groups=8, topk_groups=4)
+    torch.cuda.synchronize()
+    s_gpu, idx_gpu = s.cpu().numpy(), idx.cpu().numpy()
+    want = route.select_topk_grouped(s_gpu, b, w.k, 8, 4)
+    assert np.array_equal(idx_gpu, want)
+    np.testing.assert_allclose(gate.cpu().numpy(), route.gates(s_gpu, want), rtol=2e-6, atol=1e-7)
+    assert max(len(set((r // 32).tolist())) for r in idx_gpu) <= 4
+    assert np.any(np.sort(idx_gpu, 1) != np.sort(route.select_topk(s_gpu, b, w.k), 1))
+    s64 = route.router_scores(synth.as_f64(xb), synth.as_f64(wrb))
+    assert np.max(np.abs(s_gpu - s64)) < 1e-5
+
+
 # --------------------------------------------------------------------------- permutation
 
 

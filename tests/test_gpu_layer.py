@@ -116,6 +116,43 @@ def test_layer_small_variants(T, H, N, k, I):
     _check_small(lay, weights, y, args, k)
 
 
+def test_layer_tiny_group_limited():
+    """The tiny layer with group-limited routing: 16 experts in 4 groups of
+    4, the best 2 groups eligible, top-2 -- through MoELayer, against the
+    oracle layer with the same rule."""
+    moe = _moe()
+    w = synth.WORKLOADS["tiny"]
+    x_b = synth.generate(w.x_spec(), w.seed)
+    wr_b = w.router_weight()
+    w1_b = synth.generate(w.w1_spec(), w.seed)
+    w2_b = synth.generate(w.w2_spec(), w.seed)
+    b = w.bias()
+    log("layer tiny group-limited G=4 M=2")
+    weights = moe.MoEWeights(bf16_to_dev(wr_b), to_dev(b.copy()), w1_bf16=bf16_to_dev(w1_b),
+                             w2_bf16=bf16_to_dev(w2_b))
+    lay = moe.MoELayer(weights, w.T, w.k, w.gamma, n_groups=4, topk_groups=2)
+    y = bf16_values(lay.forward(bf16_to_dev(x_b)))
+    torch.cuda.synchronize()
+    args = (synth.as_f64(x_b), synth.as_f64(wr_b), b, synth.as_f64(w1_b), synth.as_f64(w2_b),
+            w.k, w.gamma)
+    # selection on the GPU's own scores is the group-limited rule, bit-exact
+    s_gpu = lay.scores.cpu().numpy()
+    idx = lay.idx.cpu().numpy()
+    assert np.array_equal(idx, route.select_topk_grouped(s_gpu, b, w.k, 4, 2))
+    q = olayer.moe_layer(*args, precision="Q", idx=idx)
+    assert np.array_equal(lay.counts.cpu().numpy(), q["counts"])
+    assert np.array_equal(lay.row_of.cpu().numpy(), q["row_of"])
+    assert np.array_equal(weights.bias.cpu().numpy(), q["bias"])
+    assert rel_l2(y, q["y"]) <= E2E_Q_BAR
+    d = olayer.moe_layer(*args, precision="D", idx=idx)
+    assert max_rel(y, d["y"]) <= D_BAR
+    # and the oracle's own group-limited routing agrees wherever the float64
+    # group and expert margins are clear of the router's float32 error
+    mine = olayer.moe_layer(*args, precision="Q", n_groups=4, topk_groups=2)["idx"]
+    agree = np.all(np.sort(mine, 1) == np.sort(idx, 1), axis=1)
+    assert agree.mean() > 0.95
+
+
 def test_layer_zero_input():
     w = synth.WORKLOADS["tiny"]
     zero = np.zeros((w.T, w.H), np.uint16)

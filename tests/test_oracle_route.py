@@ -141,3 +141,91 @@ def test_margin():
     b = np.array([0.0, 0.0, 0.05, 0.0])
     assert abs(route.topk_margin(s, b, 2)[0] - (0.5 - 0.45)) < 1e-15
     assert route.topk_margin(s, b, 4)[0] == np.inf
+
+
+# ---------------------------------------------------------------- group-limited selection
+# Sources: "DeepSeek-V3, explained.", recipe step 5 (nodes ranked by the sum of
+# the highest affinities they hold, the 8 experts taken from the top 4 nodes);
+# "DeepSeek-V3 Technical Report" (deepforge), "Balancing without a balance
+# loss" (at most 4 nodes, chosen by the sum of each node's top K_r / M scores).
+
+
+def _brute_grouped(key, k, G, M):
+    """Enumerate every set of M groups, keep the sets whose minimum group score
+    beats (or ties with a lower index) every excluded group, and take the top k
+    keys inside the winning set -- written independently of the oracle."""
+    N = key.size
+    gs = N // G
+    r = k // M
+    scores = []
+    for g in range(G):
+        top = sorted(key[g * gs:(g + 1) * gs].tolist(), reverse=True)[:r]
+        acc = np.float32(top[0])
+        for v in top[1:]:
+            acc = np.float32(acc + np.float32(v))
+        scores.append(acc)
+    best = None
+    for groups in itertools.combinations(range(G), M):
+        ok = all((scores[a] > scores[b]) or (scores[a] == scores[b] and a < b)
+                 for a in groups for b in range(G) if b not in groups)
+        if ok:
+            assert best is None
+            best = groups
+    cand = [e for e in range(N) if e // gs in best]
+    cand.sort(key=lambda e: (-float(key[e]), e))
+    return cand[:k]
+
+
+@pytest.mark.parametrize("N,G,M,k", [(16, 4, 2, 4), (16, 8, 4, 8), (24, 6, 3, 3), (32, 8, 4, 8)])
+def test_grouped_topk_matches_brute_force(N, G, M, k):
+    rng = np.random.default_rng(N * 100 + G * 10 + M)
+    s = rng.uniform(0, 1, (60, N)).astype(np.float32)
+    b = rng.uniform(-0.2, 0.2, N).astype(np.float32)
+    s[::7] = np.round(s[::7] * 4) / 4          # plenty of exact ties
+    idx = route.select_topk_grouped(s, b, k, G, M)
+    key = route.biased_keys(s, b)
+    for t in range(s.shape[0]):
+        assert idx[t].tolist() == _brute_grouped(key[t], k, G, M), t
+
+
+def test_grouped_topk_reduces_to_plain_topk():
+    rng = np.random.default_rng(8)
+    s = rng.uniform(0, 1, (50, 64)).astype(np.float32)
+    b = rng.uniform(-0.1, 0.1, 64).astype(np.float32)
+    plain = route.select_topk(s, b, 8)
+    assert np.array_equal(route.select_topk_grouped(s, b, 8, 8, 8), plain)   # every group
+    assert np.array_equal(route.select_topk_grouped(s, b, 8, 1, 1), plain)   # one group
+
+
+def test_grouped_topk_limits_the_groups_and_keeps_gates_unbiased():
+    """A token whose plain top-8 spans 8 groups gets 8 experts from 4 groups;
+    the chosen experts are the top keys of the chosen groups; the gates are
+    the unbiased scores normalised, whatever the bias."""
+    N, G, M, k = 256, 8, 4, 8
+    s = np.full((1, N), 0.1, np.float32)
+    # group g holds one strong expert 32 g (score 0.9 - 0.01 g) and, for even
+    # g, a second one of 0.5: even groups score higher by their second key
+    for g in range(G):
+        s[0, 32 * g] = 0.9 - 0.01 * g
+        if g % 2 == 0:
+            s[0, 32 * g + 1] = 0.5
+    b = np.zeros(N, np.float32)
+    plain = route.select_topk(s, b, k)[0]
+    assert len({e // 32 for e in plain}) == 8
+    idx = route.select_topk_grouped(s, b, k, G, M)[0]
+    assert {e // 32 for e in idx} == {0, 2, 4, 6}
+    assert idx.tolist() == [0, 64, 128, 192, 1, 65, 129, 193]
+    # a bias that only reorders inside the chosen set leaves the gates alone
+    b2 = b.copy()
+    b2[[0, 64, 128, 192, 1, 65, 129, 193]] += 0.001
+    idx2 = route.select_topk_grouped(s, b2, k, G, M)
+    g1 = route.gates(s, idx[None, :])
+    g2 = route.gates(s, idx2)
+    assert sorted(idx2[0].tolist()) == sorted(idx.tolist())
+    np.testing.assert_allclose(np.sort(g1[0]), np.sort(g2[0]), rtol=0, atol=0)
+    # a large bias on a weak group's expert pulls that group in (selection
+    # uses the biased keys, group ranking included)
+    b3 = b.copy()
+    b3[32 * 7 + 5] = 2.0
+    idx3 = route.select_topk_grouped(s, b3, k, G, M)[0]
+    assert 32 * 7 + 5 in idx3 and 7 in {e // 32 for e in idx3}
