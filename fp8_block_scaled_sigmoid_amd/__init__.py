@@ -63,6 +63,7 @@ def lib():
             "moe_grouped_gemm_fp8": [ctypes.POINTER(GemmArgs), _P],
             "moe_combine": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P],
             "moe_bias_update": [_P, _P, _I, _I, _I, ctypes.c_float, _P],
+            "moe_seq_balance_loss": [_P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -240,6 +241,20 @@ def moe_bias_update(bias, counts, T, k, gamma, stream=None):
     _check("moe_bias_update", lib().moe_bias_update(_ptr(bias), _ptr(counts), N, T, k,
                                                     float(gamma), _stream(stream)))
     return bias
+
+
+def moe_seq_balance_loss(idx, gate, seq_offsets, n_experts, alpha=1e-4, loss=None, stream=None):
+    """Sequence-wise balance statistic per sequence: idx int32 [T,k], gate
+    float32 [T,k], seq_offsets int32 [S+1] (device) -> loss float32 [S]."""
+    T, k = idx.shape
+    _dev(idx, torch.int32, "idx"), _dev(gate, torch.float32, "gate")
+    _dev(seq_offsets, torch.int32, "seq_offsets")
+    S = seq_offsets.numel() - 1
+    loss = torch.empty(max(S, 0), dtype=torch.float32, device=idx.device) if loss is None else loss
+    _check("moe_seq_balance_loss", lib().moe_seq_balance_loss(
+        _ptr(idx), _ptr(gate), _ptr(seq_offsets), S, T, n_experts, k, alpha, _ptr(loss),
+        _stream(stream)))
+    return loss
 
 
 # ---------------------------------------------------------------------------

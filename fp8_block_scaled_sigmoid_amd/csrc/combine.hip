@@ -96,7 +96,67 @@ __global__ __launch_bounds__(256) void bias_update_kernel(float* __restrict__ bi
   }
 }
 
+// Sequence-wise balance statistic ("DeepSeek-V3: Auxiliary-Loss-Free MoE Load
+// Balancing, ...", section III, "The one small loss that remains"): per
+// sequence s of T_s tokens, L = alpha * sum_i f_i P_i with f_i = N / (k T_s) *
+// count_i (normalised load) and P_i = (1 / T_s) * sum of the gates expert i
+// received (mean gate mass).  One workgroup per sequence; counts and gate
+// masses are integers (gates in units of 2^-32), so the LDS atomics give the
+// same sums in any order, and the final sum over experts is a fixed tree in
+// double.
+__global__ __launch_bounds__(256) void seq_balance_kernel(
+    const int32_t* __restrict__ idx, const float* __restrict__ gate,
+    const int32_t* __restrict__ seq_off, int T, int N, int k, float alpha,
+    float* __restrict__ loss) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  unsigned long long* mass = reinterpret_cast<unsigned long long*>(smem);   // [N]
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(smem + (size_t)N * 8);      // [N]
+  __shared__ double wsum[4];
+  const int s = blockIdx.x, tid = threadIdx.x;
+  int t0 = seq_off[s], t1 = seq_off[s + 1];
+  t0 = t0 < 0 ? 0 : (t0 > T ? T : t0);
+  t1 = t1 < t0 ? t0 : (t1 > T ? T : t1);
+  for (int e = tid; e < N; e += 256) {
+    mass[e] = 0ull;
+    cnt[e] = 0u;
+  }
+  __syncthreads();
+  const long long n = (long long)(t1 - t0) * k;
+  for (long long i = tid; i < n; i += 256) {
+    const long long a = (long long)t0 * k + i;
+    int e = idx[a];
+    e = e < 0 ? 0 : (e >= N ? N - 1 : e);
+    const double g = (double)gate[a];
+    atomicAdd(&cnt[e], 1u);
+    atomicAdd(&mass[e], (unsigned long long)__builtin_rint(g * 4294967296.0));
+  }
+  __syncthreads();
+  double term = 0.0;
+  for (int e = tid; e < N; e += 256) term += (double)cnt[e] * (double)mass[e];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) term += __shfl_xor(term, o, 64);
+  if ((tid & 63) == 0) wsum[tid >> 6] = term;
+  __syncthreads();
+  if (tid == 0) {
+    const double tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    const int Ts = t1 - t0;
+    loss[s] = Ts > 0 ? (float)((double)alpha * N / ((double)k * Ts) * (tot * 0x1p-32) / Ts) : 0.0f;
+  }
+}
+
 }  // namespace
+
+extern "C" moe_status_t moe_seq_balance_loss(const int32_t* topk_idx, const float* topk_gate,
+                                             const int32_t* seq_offsets, int n_seq, int T, int N,
+                                             int k, float alpha, float* loss, hipStream_t stream) {
+  if (n_seq < 0 || T < 0 || N < 1 || N > 1024 || k < 1 || k > 32) return MOE_ERR_SHAPE;
+  if (n_seq == 0) return MOE_OK;
+  if (!seq_offsets || !loss || (T > 0 && (!topk_idx || !topk_gate))) return MOE_ERR_NULL;
+  if (moe_status_t st = check_device()) return st;
+  hipLaunchKernelGGL(seq_balance_kernel, dim3(n_seq), dim3(256), (size_t)N * 12, stream, topk_idx,
+                     topk_gate, seq_offsets, T, N, k, alpha, loss);
+  return launch_status();
+}
 
 extern "C" moe_status_t moe_combine(const void* out_rows_bf16, const float* gate,
                                     const int32_t* row_of, int shared_row0, int T, int H, int k,

@@ -219,6 +219,22 @@ moe_status_t moe_bias_update(float* bias, const int32_t* counts, int N, int T, i
                              hipStream_t stream);
 
 /* Human-readable name of a status code (static string). */
+/*
+ * Sequence-wise balance statistic ([TP] section III, "The one small loss that
+ * remains"; [VE] recipe step 4): for each sequence s (tokens seq_offsets[s] ..
+ * seq_offsets[s+1]-1, T_s of them, clamped into [0, T]),
+ *   loss[s] = alpha * sum_i f_i P_i,  f_i = N / (k T_s) * #{(t,j): idx = i},
+ *   P_i = (1 / T_s) * sum of the gates expert i received;
+ * 0 for an empty sequence.  topk_idx int32 [T,k] and topk_gate float [T,k] as
+ * moe_route_topk writes them (idx entries outside [0, N) are clamped),
+ * seq_offsets int32 [n_seq + 1] device, loss float [n_seq].  Gates are summed
+ * in units of 2^-32 and the result is formed in double, so it is
+ * deterministic.  Requires 1 <= N <= 1024, 1 <= k <= 32.
+ */
+moe_status_t moe_seq_balance_loss(const int32_t* topk_idx, const float* topk_gate,
+                                  const int32_t* seq_offsets, int n_seq, int T, int N, int k,
+                                  float alpha, float* loss, hipStream_t stream);
+
 const char* moe_status_str(moe_status_t status);
 /* hipError_t of the most recent MOE_ERR_HIP on this thread (0 if none). */
 int moe_last_hip_error(void);

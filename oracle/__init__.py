@@ -24,10 +24,11 @@ a float32 rounding point).  It follows these pages, cited by title and section:
 Modules:
   e4m3     OCP E4M3 codec, written twice (table search and arithmetic).
   quant    1x128 activation and 128x128 weight quantisers.
-  route    sigmoid router, biased top-k, unbiased gates.
+  route    sigmoid router, biased top-k (plain and group-limited), unbiased gates.
   permute  per-expert counts, offsets and the stable token permutation.
   ffn      block-scaled FP8 GEMM, SwiGLU expert, combine (two precisions).
   bias     sign-based bias update.
+  balance  sequence-wise balance statistic (f_i P_i per sequence).
   layer    the whole layer chained from the pieces above.
 
 Parity status: every function above is pinned by ``tests/test_oracle_*.py``

@@ -92,6 +92,10 @@ def test_validation_before_any_launch(lib):
     assert lib.moe_combine(None, None, None, 0, 4, 12, 2, None, None, None) == 2   # H % 8
     lib.moe_bias_update.argtypes = [P, P, I, I, I, ctypes.c_float, P]
     assert lib.moe_bias_update(None, None, 4, 1, 1, 0.1, None) == 1
+    lib.moe_seq_balance_loss.argtypes = [P, P, P, I, I, I, I, ctypes.c_float, P, P]
+    assert lib.moe_seq_balance_loss(None, None, None, 2, 8, 2000, 2, 1e-4, None, None) == 2
+    assert lib.moe_seq_balance_loss(None, None, None, 0, 8, 16, 2, 1e-4, None, None) == 0
+    assert lib.moe_seq_balance_loss(None, None, dummy, 2, 8, 16, 2, 1e-4, dummy, None) == 1
     lib.moe_permute_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_permute_workspace_bytes.argtypes = [I, I, I]
     assert lib.moe_permute_workspace_bytes(513, 256, 8) == 3 * 256 * 4

@@ -7,6 +7,7 @@ import pytest
 import synth
 from helpers import (bf16_from_dev, bf16_to_dev, bf16_values, codes_agree_up_to_ties,
                      device_tensor, log, rel_l2, to_dev)
+from oracle import balance as obalance
 from oracle import bias as obias
 from oracle import e4m3, ffn, permute as opermute, quant, route
 
@@ -556,3 +557,28 @@ def test_mfma_block_sum_precision_probe():
         lost = (exact - got[i]) / 2.0 ** e
         print(f"small products 2^{e:+d}: exact {exact:.6f} mfma {got[i]:.6f} lost {lost:g}")
         assert lost == (0 if 2.0 ** e >= 8 else 7)
+
+
+# --------------------------------------------------------------------------- balance statistic
+
+
+def test_seq_balance_loss_against_oracle():
+    """Router output of the prefill workload's first 3000 tokens, cut into
+    ragged sequences (one empty): the per-sequence statistic within 1e-6 of
+    the float64 oracle, and bit-identical when run twice."""
+    moe = _moe()
+    w = synth.WORKLOADS["prefill"]
+    T = 3000
+    xb = synth.generate(w.x_spec(), w.seed, rows=np.arange(T))
+    log("moe_seq_balance_loss")
+    idx, gate, _ = moe.moe_route_topk(bf16_to_dev(xb), bf16_to_dev(w.router_weight()),
+                                      to_dev(w.bias()), w.k)
+    off = np.array([0, 1, 1000, 1000, 2047, 3000], np.int32)
+    loss = moe.moe_seq_balance_loss(idx, gate, to_dev(off), w.N)
+    loss2 = moe.moe_seq_balance_loss(idx, gate, to_dev(off), w.N)
+    torch.cuda.synchronize()
+    want = obalance.seq_balance_loss(idx.cpu().numpy(), gate.cpu().numpy(), off, w.N)
+    got = loss.cpu().numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-6, atol=0)
+    assert got[2] == 0.0
+    assert np.array_equal(got, loss2.cpu().numpy())
