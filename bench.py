@@ -32,11 +32,17 @@ KERNEL_SOURCES = [os.path.join(ROOT, "fp8_block_scaled_sigmoid_amd", "csrc", f)
 
 
 def kernel_source_hash():
+    """Hash of the GEMM kernel's source with comments and blank space removed
+    (a comment edit does not change the kernel the counters measured)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -21,23 +21,27 @@
 //     its 64 float accumulators stay in VALU registers;
 //   * the A tile (128 rows x 128 B, gathered through a_row_index), the B tile
 //     (256 x 128 B) and the 128 A scales of a K block are copied global -> LDS
-//     by the direct-to-LDS loads (global_load_lds_dwordx4), three stages deep:
-//     stage kb + 2 is requested while stage kb is consumed, and each wave waits
-//     with an explicit vmcnt for exactly the stage it needs next;
+//     by buffer-resource direct-to-LDS loads whose per-lane offset is fixed
+//     and whose K position is the scalar offset, three stages deep: stage
+//     kb + 2 is requested in parts spread over the MFMAs of stage kb, and each
+//     wave waits with an explicit vmcnt for exactly the stage it needs next;
 //   * LDS rows are 128 B; 16-byte chunk c of row r sits at chunk position
-//     c ^ ((r >> 1) & 7), so the 16 rows one ds_read_b128 phase touches cover
-//     all 64 banks once, and each direct-to-LDS load still writes 1 KiB of
-//     consecutive LDS (8 rows);
+//     c ^ ((r >> 1) & 7), and each direct-to-LDS load writes 1 KiB of
+//     consecutive LDS (8 rows); MFMA lane group lk reads K chunks lk and lk + 4
+//     (the same permutation of K for A and B), which keeps every ds_read_b128
+//     free of bank conflicts;
 //   * with the SwiGLU epilogue the B tile is the interleaved pair (gate block j,
-//     up block j) of W1: waves wn < 2 hold gate, wn >= 2 hold up; the up
-//     waves hand their accumulators to the gate waves through LDS, and the 128
-//     h columns of a row (one 1x128 quantisation tile) span two waves;
+//     up block j) of W1: waves wn < 2 hold gate, wn >= 2 hold up; each gate
+//     wave and its up partner swap half of their subtiles through LDS so all
+//     8 waves form h, and the 128 h columns of a row (one 1x128 quantisation
+//     tile) meet in LDS for the tile maximum;
 //   * every workgroup derives the tile list itself from the device-side group
 //     offsets (tiles ordered group, column tile, row tile), so the call needs no
 //     workspace and no host sync; consecutive row tiles of one (expert, column
 //     tile) are mapped to the same XCD so their weight tile is fetched from HBM
-//     once and re-read from that XCD's L2; row subtiles past the end of a
-//     group's rows skip their MFMAs.
+//     once and re-read from that XCD's L2; in a group's last row tile, 16-row
+//     subtiles past the group's end skip their MFMAs (the K loop is compiled
+//     for each count of live subtiles).
 #include <type_traits>
 
 #include "common.h"
