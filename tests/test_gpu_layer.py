@@ -279,6 +279,80 @@ def test_layer_v3_shape_sampled(name):
     assert np.array_equal(weights.bias.cpu().numpy(), want_b)
 
 
+def test_layer_skew_ten_batches():
+    """The skewed-load stress workload at its full size (T = 32768 per batch,
+    DeepSeek-V3 shape, Zipf(1.2) per-expert logit offsets, 1 % of the
+    activation channels x100): ten successive batches (batch b draws x with
+    seed offset b) through one MoELayer, the bias updated after each.  Every
+    batch: selection bit-exact on the GPU's own scores with the bias of that
+    batch, counts equal to the routing, the bias update bit-exact, routing and
+    activation codes against the float64 oracle on a token sample; the
+    per-expert load max/mean is printed after each batch.  Batch 0 also checks
+    the most loaded expert's FFN on a row sample."""
+    from oracle import bias as obias
+    moe = _moe()
+    w = synth.WORKLOADS["skew"]
+    weights, wr_b, b = _build_v3(w)
+    lay = moe.MoELayer(weights, w.T, w.k, w.gamma)
+    T, k, N = w.T, w.k, w.N
+    rng = np.random.default_rng(4)
+    bias = b.copy()
+    ratios = []
+    for batch in range(w.batches):
+        x = device_tensor(w.x_spec(batch), w.seed)
+        log(f"skew batch {batch}")
+        y = lay.forward(x)
+        torch.cuda.synchronize()
+        s_gpu = lay.scores.cpu().numpy()
+        idx = lay.idx.cpu().numpy()
+        counts = lay.counts.cpu().numpy()
+        assert np.array_equal(idx, route.select_topk(s_gpu, bias, k))
+        np.testing.assert_allclose(lay.gate.cpu().numpy(), route.gates(s_gpu, idx), rtol=2e-6,
+                                   atol=1e-7)
+        assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=N))
+        new_bias = obias.bias_update(bias, counts, T, k, w.gamma)
+        assert np.array_equal(weights.bias.cpu().numpy(), new_bias)
+        # routing and activation codes against the oracle on 256 sampled tokens
+        sample = np.sort(rng.choice(T, 256, replace=False))
+        xb = synth.generate(w.x_spec(batch), w.seed, rows=sample)
+        s64 = route.router_scores(synth.as_f64(xb), synth.as_f64(wr_b))
+        assert np.max(np.abs(s_gpu[sample] - s64)) < 1e-5
+        clear = route.topk_margin(s64, bias, k) > 3e-5
+        assert clear.mean() > 0.95
+        idx_o = route.select_topk(s64.astype(np.float32), bias, k)
+        assert np.array_equal(idx[sample][clear], idx_o[clear])
+        xq_o, xd_o = quant.quant_1x128(synth.as_f64(xb))
+        assert np.array_equal(lay.xq.cpu().numpy()[sample], xq_o)
+        assert np.array_equal(lay.xd.cpu().numpy()[sample], xd_o)
+        ratio = counts.max() / counts.mean()
+        ratios.append(ratio)
+        print(f"batch {batch}: per-expert load max/mean {ratio:.2f}, "
+              f"experts above 10x mean {(counts > 10 * counts.mean()).sum()}, "
+              f"empty experts {(counts == 0).sum()}")
+        if batch == 0:
+            g = int(np.argmax(counts))
+            offsets = lay.offsets.cpu().numpy()
+            token_of = lay.token_of.cpu().numpy()
+            r0 = int(offsets[g])
+            rows = r0 + np.sort(rng.choice(int(counts[g]), 48, replace=False))
+            toks = token_of[rows]
+            xr = synth.generate(w.x_spec(batch), w.seed, rows=toks)
+            xq_r, xd_r = quant.quant_1x128(synth.as_f64(xr))
+            log(f"oracle skew expert {g} rows {rows.size}")
+            w1q, w1d, w2q, w2d = _expert_oracle(w, g)
+            resq = ffn.expert_ffn(xq_r, xd_r, w1q, w1d, w2q, w2d, "Q")
+            resd = ffn.expert_ffn(xq_r, xd_r, w1q, w1d, w2q, w2d, "D")
+            check_h(lay.hq.cpu().numpy()[rows], lay.hd.cpu().numpy()[rows], resq["h"])
+            got = bf16_values(lay.out_rows[torch.from_numpy(rows).cuda()])
+            assert rel_l2(got, resq["out"]) <= E2E_Q_BAR
+            assert max_rel(got, resd["out"]) <= D_BAR
+        bias = new_bias
+        del y
+    # the Zipf offsets give a strongly skewed load (design intent: a few
+    # experts above 10x the mean)
+    assert ratios[0] > 10
+
+
 @pytest.mark.parametrize("T,H,N,k,I", [(64, 256, 16, 2, 128), (200, 1024, 8, 3, 512),
                                        (48, 7168, 4, 2, 2048)])
 def test_gemm2_combine_rounding_faithful(T, H, N, k, I):
