@@ -81,8 +81,8 @@ def parse():
 def cpu_baseline(w, sample_tokens=None):
     """The oracle, untuned, on a bounded sample of the same workload.
 
-    Sample: the first `sample_tokens` tokens of the batch (default: all of
-    it).  Routing, the activation quantisation, the permutation, the combine
+    Sample: the first `sample_tokens` tokens of the batch (default: up to
+    8192).  Routing, the activation quantisation, the permutation, the combine
     and the bias update run on the whole sample; the expert FFN runs on every
     sample row of the shared expert and of the two routed experts with the
     most sample rows, and its per-row time is scaled to the sample's T*(k+1)
@@ -95,7 +95,7 @@ def cpu_baseline(w, sample_tokens=None):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
-    S = w.T if sample_tokens is None else min(sample_tokens, w.T)
+    S = min(w.T, 8192) if sample_tokens is None else min(sample_tokens, w.T)
     x = synth.as_f64(synth.generate(w.x_spec(), w.seed, rows=np.arange(S)))
     wr = synth.as_f64(w.router_weight())
     b = w.bias()
@@ -135,6 +135,100 @@ def cpu_baseline(w, sample_tokens=None):
             "measured_s": round(t_route + t_ffn + t_tail, 3)}
 
 
+def cpu_baseline_routing(w):
+    """The oracle's routing path (router, biased top-k, gates, counts and
+    permutation, bias update) on the whole routing batch, on the host."""
+    import synth
+    from oracle import bias as obias, permute as operm, route
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    x = synth.as_f64(synth.generate(w.x_spec(), w.seed))
+    wr = synth.as_f64(w.router_weight())
+    b = w.bias()
+    t0 = time.perf_counter()
+    s64, s32, idx, gate = route.route(x, wr, b, w.k)
+    counts, offsets, row_of, token_of = operm.permute(idx, w.N, False)
+    obias.bias_update(b, counts, w.T, w.k, w.gamma)
+    dt = time.perf_counter() - t0
+    return {"value": w.T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"all {w.T} tokens of the {w.name} batch (router, top-k, gates, counts, "
+                      f"permutation, bias update)", "measured_s": round(dt, 3)}
+
+
+def bench_routing(args, w, moe, torch, gen, wr, bias, st):
+    """The routing-only workload: a step is the router with biased top-k and
+    gates, the counts and permutation maps, and the bias update."""
+    dev = wr.device
+    T, H, N, k = w.T, w.H, w.N, w.k
+    x = gen(w.x_spec())
+    e = dict(device=dev)
+    scores = torch.empty(T, N, dtype=torch.float32, **e)
+    idx = torch.empty(T, k, dtype=torch.int32, **e)
+    gate = torch.empty(T, k, dtype=torch.float32, **e)
+    rws = torch.empty(max(moe.moe_route_workspace_bytes(T, H, N), 16), dtype=torch.uint8, **e)
+    maps = (torch.empty(N, dtype=torch.int32, **e), torch.empty(N + 2, dtype=torch.int32, **e),
+            torch.empty(T, k, dtype=torch.int32, **e), torch.empty(T * k, dtype=torch.int32, **e))
+    pws = torch.empty(max(moe.moe_permute_workspace_bytes(T, N, k), 16), dtype=torch.uint8, **e)
+    names = ["route", "permute", "bias"]
+    fns = [lambda: moe.moe_route_topk(x, wr, bias, k, scores=scores, idx=idx, gate=gate, ws=rws),
+           lambda: moe.moe_permute(idx, N, False, out=maps, ws=pws),
+           lambda: moe.moe_bias_update(bias, maps[0], T, k, w.gamma)]
+
+    def step(evs=None):
+        for i, f in enumerate(fns):
+            if evs is not None:
+                evs[i][0].record(st)
+            f()
+            if evs is not None:
+                evs[i][1].record(st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(args.steps):
+        step()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    per = {n: [] for n in names}
+    for _ in range(args.steps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in names]
+        step(evs)
+        torch.cuda.synchronize()
+        for n, (a, b) in zip(names, evs):
+            per[n].append(a.elapsed_time(b))
+    kern = {n: float(np.mean(v)) for n, v in per.items()}
+    route_bytes = T * H * 2 + N * H * 2 + N * 4 + T * N * 4 + T * k * 8
+    gbs = route_bytes / (kern["route"] * 1e-3) / 1e9
+    res = {
+        "metric": "MoE routing tokens/s (sigmoid router + biased top-k + permutation + bias "
+                  "update) at V3 shape, 1 GPU",
+        "value": round(T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 (fp32 accumulate)",
+        "data": "synthetic (seeded counter-based generator, generated on the device)",
+        "config": {"workload": f"{w.name}: T={T} tokens, hidden {H}, {N} experts top-{k}, "
+                               f"bias U(-0.05, 0.05), gamma {w.gamma}",
+                   "T": T, "H": H, "N": N, "k": k},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "route_partial_kernel + route_finish_kernel",
+                     "kernel_avg_ms": round(kern["route"], 4),
+                     "algorithmic_bytes_per_launch": route_bytes},
+        "kernel_ms": {n: round(v, 4) for n, v in kern.items()},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_routing(w)
+    print(json.dumps(res))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -158,6 +252,9 @@ def main():
     wr = torch.from_numpy(w.router_weight().view(np.int16)).view(torch.bfloat16).to(dev)
     bias = torch.from_numpy(w.bias().copy()).to(dev)
     st = torch.cuda.current_stream()
+    if not w.with_experts:
+        bench_routing(args, w, moe, torch, gen, wr, bias, st)
+        return
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     w1 = gen(w.w1_spec())
     e0.record(st)
@@ -176,10 +273,14 @@ def main():
     torch.cuda.empty_cache()
     weights = moe.MoEWeights(wr, bias, w1q=w1q, w1d=w1d, w2q=w2q, w2d=w2d)
     lay = moe.MoELayer(weights, w.T, w.k, w.gamma, device=dev)
-    x = gen(w.x_spec())
+    # the batches of the workload (one for most; the skewed-load workload has
+    # ten, batch b drawn with seed offset b); step i runs batch i % batches
+    xs = [gen(w.x_spec(b)) for b in range(w.batches)]
+    cur = {"i": 0}
 
     names = ["route", "permute", "quant_x", "gemm1", "gemm2", "combine", "bias"]
-    fns = [lambda: lay.route(x), lay.permute, lambda: lay.quant_x(x), lay.gemm1, lay.gemm2,
+    fns = [lambda: lay.route(xs[cur["i"] % len(xs)]), lay.permute,
+           lambda: lay.quant_x(xs[cur["i"] % len(xs)]), lay.gemm1, lay.gemm2,
            lay.combine, lay.bias_update]
 
     def step(evs=None):
@@ -189,6 +290,7 @@ def main():
             f()
             if evs is not None:
                 evs[i][1].record(st)
+        cur["i"] += 1
 
     for _ in range(args.warmup):
         step()
@@ -204,7 +306,9 @@ def main():
     ms_total = e0.elapsed_time(e1)
     ms_step = ms_total / args.steps
     # per-kernel timing: the same steps again with events around each launch
+    # (and the per-expert load max/mean of each step's batch, read after it)
     per = {n: [] for n in names}
+    load_ratio = []
     for _ in range(args.steps):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in names]
@@ -212,6 +316,8 @@ def main():
         torch.cuda.synchronize()
         for n, (a, b) in zip(names, evs):
             per[n].append(a.elapsed_time(b))
+        c = lay.counts.cpu().numpy()
+        load_ratio.append(round(float(c.max() / c.mean()), 3))
     kern = {n: float(np.mean(v)) for n, v in per.items()}
 
     R, G, T, H, I = w.R, w.G, w.T, w.H, w.I
@@ -281,6 +387,8 @@ def main():
         "gemm_frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
         "kernel_ms": {n: round(v, 4) for n, v in kern.items()},
         "hbm_phases": phases,
+        "expert_load_max_over_mean": load_ratio[: max(w.batches, 1)] if w.batches > 1
+        else load_ratio[-1],
         "weight_quant_ms": round(t_wq1 + t_wq2, 3),
         "wall_s_timed": round(wall, 3),
     }

@@ -149,11 +149,14 @@ __device__ __forceinline__ uint32_t group_excluded(const float (&key)[PER], int 
 __device__ __forceinline__ float sigmoidf_acc(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 // Number of H slices for T tokens: enough workgroups for about one per
-// compute unit, at most one slice per 64-wide chunk.
+// compute unit, at most one slice per 64-wide chunk, and at most 16 (the
+// partial logits, S * T * N floats written and read back, must stay small
+// next to x when T is small).
 int route_splits(int T, int H) {
   const int nc = H / kRKc;
   const int tiles = (T + kRT - 1) / kRT;
   int S = (256 + tiles - 1) / tiles;
+  if (S > 16) S = 16;
   return S < 1 ? 1 : (S > nc ? nc : S);
 }
 
