@@ -10,6 +10,10 @@ device, resident in HBM before the timed region.
 
 Prints ONE JSON line.  Default workload: the DeepSeek-V3-shaped layer at
 prefill size (T = 8192, H 7168, 256 routed experts top-8 + 1 shared, I 2048).
+Other workloads: decode (T = 512), skew (T = 32768, ten batches cycled, load
+max/mean reported), tiny, and routing (T = 16384: router, top-k, permutation
+and bias update only).  The timed region is K steps with an event pair around
+every launch on the launch stream; per-kernel times are the means of those.
 """
 import argparse
 import json
@@ -189,21 +193,17 @@ def bench_routing(args, w, moe, torch, gen, wr, bias, st):
         step()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in names] for _ in range(args.steps)]
     e0.record(st)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(evs[i])
     e1.record(st)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
-    per = {n: [] for n in names}
-    for _ in range(args.steps):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in names]
-        step(evs)
-        torch.cuda.synchronize()
-        for n, (a, b) in zip(names, evs):
-            per[n].append(a.elapsed_time(b))
-    kern = {n: float(np.mean(v)) for n, v in per.items()}
+    kern = {n: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1])
+                              for i in range(args.steps)]))
+            for j, n in enumerate(names)}
     route_bytes = T * H * 2 + N * H * 2 + N * 4 + T * N * 4 + T * k * 8
     gbs = route_bytes / (kern["route"] * 1e-3) / 1e9
     res = {
@@ -295,30 +295,29 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # whole-step timing (no per-kernel events inside)
+    # the timed region: K steps with an event pair around every launch (all
+    # on the launch stream), bracketed by one more pair for the whole region
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in names] for _ in range(args.steps)]
     t0 = time.perf_counter()
     e0.record(st)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(evs[i])
     e1.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = e0.elapsed_time(e1)
     ms_step = ms_total / args.steps
-    # per-kernel timing: the same steps again with events around each launch
-    # (and the per-expert load max/mean of each step's batch, read after it)
-    per = {n: [] for n in names}
+    per = {n: [evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(args.steps)]
+           for j, n in enumerate(names)}
+    kern = {n: float(np.mean(v)) for n, v in per.items()}
+    # after the timed region: the per-expert load max/mean of the workload's
+    # batches (one more pass over them, each followed by a read of the counts)
     load_ratio = []
-    for _ in range(args.steps):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in names]
-        step(evs)
-        torch.cuda.synchronize()
-        for n, (a, b) in zip(names, evs):
-            per[n].append(a.elapsed_time(b))
+    for _ in range(max(w.batches, 1)):
+        step()
         c = lay.counts.cpu().numpy()
         load_ratio.append(round(float(c.max() / c.mean()), 3))
-    kern = {n: float(np.mean(v)) for n, v in per.items()}
 
     R, G, T, H, I = w.R, w.G, w.T, w.H, w.I
     g1_flops = 2.0 * R * H * 2 * I
@@ -387,8 +386,7 @@ def main():
         "gemm_frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
         "kernel_ms": {n: round(v, 4) for n, v in kern.items()},
         "hbm_phases": phases,
-        "expert_load_max_over_mean": load_ratio[: max(w.batches, 1)] if w.batches > 1
-        else load_ratio[-1],
+        "expert_load_max_over_mean": load_ratio if w.batches > 1 else load_ratio[-1],
         "weight_quant_ms": round(t_wq1 + t_wq2, 3),
         "wall_s_timed": round(wall, 3),
     }
