@@ -14,6 +14,9 @@ Other workloads: decode (T = 512), skew (T = 32768, ten batches cycled, load
 max/mean reported), tiny, and routing (T = 16384: router, top-k, permutation
 and bias update only).  The timed region is K steps with an event pair around
 every launch on the launch stream; per-kernel times are the means of those.
+--router-fp8 swaps in the opt-in FP8 router (x quantised before routing); the
+routing workload also times the other router on the same batch and reports
+how many tokens both send to the same expert set.
 """
 import argparse
 import json
@@ -76,6 +79,9 @@ def parse():
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "decode", "skew", "routing", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--router-fp8", action="store_true",
+                    help="the opt-in FP8 router (x quantised 1x128 first, Wr 128x128) in place "
+                         "of the bf16 one")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also time a plain 2 GiB device copy (reference for the HBM "
                          "byte counters and the measured copy bandwidth)")
@@ -162,6 +168,18 @@ def cpu_baseline_routing(w):
                       f"permutation, bias update)", "measured_s": round(dt, 3)}
 
 
+def route_bytes_of(T, H, N, k, fp8):
+    """Algorithmic HBM bytes of the routing step: x and Wr read once (bf16, or
+    for the FP8 router x bf16 read by the quantiser, its codes and scales
+    written and read back, Wr codes and scales read), bias read, scores and
+    (index, gate) pairs written."""
+    out = N * 4 + T * N * 4 + T * k * 8
+    if not fp8:
+        return out + T * H * 2 + N * H * 2
+    xq = T * H + T * (H // 128) * 4
+    return out + T * H * 2 + 2 * xq + N * H + (N // 128) * (H // 128) * 4
+
+
 def bench_routing(args, w, moe, torch, gen, wr, bias, st):
     """The routing-only workload: a step is the router with biased top-k and
     gates, the counts and permutation maps, and the bias update."""
@@ -176,8 +194,23 @@ def bench_routing(args, w, moe, torch, gen, wr, bias, st):
     maps = (torch.empty(N, dtype=torch.int32, **e), torch.empty(N + 2, dtype=torch.int32, **e),
             torch.empty(T, k, dtype=torch.int32, **e), torch.empty(T * k, dtype=torch.int32, **e))
     pws = torch.empty(max(moe.moe_permute_workspace_bytes(T, N, k), 16), dtype=torch.uint8, **e)
+    xq = torch.empty(T, H, dtype=torch.uint8, **e)
+    xd = torch.empty(T, H // 128, dtype=torch.float32, **e)
+    wq, wd = moe.fp8_quant_128x128(wr)          # per weight update, outside the timed region
+    wq, wd = wq[0], wd[0]
+
+    def route_bf16(out_idx):
+        moe.moe_route_topk(x, wr, bias, k, scores=scores, idx=out_idx, gate=gate, ws=rws)
+
+    def route_fp8(out_idx):
+        moe.fp8_quant_1x128(x, q=xq, d=xd)
+        moe.moe_route_topk_fp8(xq, xd, wq, wd, bias, k, scores=scores, idx=out_idx, gate=gate,
+                               ws=rws)
+
+    main_route, other_route = (route_fp8, route_bf16) if args.router_fp8 else \
+        (route_bf16, route_fp8)
     names = ["route", "permute", "bias"]
-    fns = [lambda: moe.moe_route_topk(x, wr, bias, k, scores=scores, idx=idx, gate=gate, ws=rws),
+    fns = [lambda: main_route(idx),
            lambda: moe.moe_permute(idx, N, False, out=maps, ws=pws),
            lambda: moe.moe_bias_update(bias, maps[0], T, k, w.gamma)]
 
@@ -204,25 +237,43 @@ def bench_routing(args, w, moe, torch, gen, wr, bias, st):
     kern = {n: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1])
                               for i in range(args.steps)]))
             for j, n in enumerate(names)}
-    route_bytes = T * H * 2 + N * H * 2 + N * 4 + T * N * 4 + T * k * 8
+    route_bytes = route_bytes_of(T, H, N, k, args.router_fp8)
     gbs = route_bytes / (kern["route"] * 1e-3) / 1e9
+    # the other router on the same batch and bias (after the timed region):
+    # its time, and the fraction of tokens that both send to the same experts
+    idx_other = torch.empty_like(idx)
+    other_route(idx_other)
+    e0.record(st)
+    for _ in range(args.steps):
+        other_route(idx_other)
+    e1.record(st)
+    torch.cuda.synchronize()
+    main_route(idx)
+    same = (idx.sort(dim=1).values == idx_other.sort(dim=1).values).all(dim=1)
+    agree = float(same.float().mean().item())
     res = {
         "metric": "MoE routing tokens/s (sigmoid router + biased top-k + permutation + bias "
                   "update) at V3 shape, 1 GPU",
         "value": round(T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 (fp32 accumulate)",
+        "dtype": ("fp8_e4m3 router" if args.router_fp8 else "bf16") + " (fp32 accumulate)",
         "data": "synthetic (seeded counter-based generator, generated on the device)",
         "config": {"workload": f"{w.name}: T={T} tokens, hidden {H}, {N} experts top-{k}, "
                                f"bias U(-0.05, 0.05), gamma {w.gamma}",
-                   "T": T, "H": H, "N": N, "k": k},
+                   "T": T, "H": H, "N": N, "k": k,
+                   "router": "fp8" if args.router_fp8 else "bf16"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "route_partial_kernel + route_finish_kernel",
+                     "kernel": ("fp8_quant_1x128 + route_partial_fp8_kernel + route_finish_kernel"
+                                if args.router_fp8 else
+                                "route_partial_kernel + route_finish_kernel"),
                      "kernel_avg_ms": round(kern["route"], 4),
                      "algorithmic_bytes_per_launch": route_bytes},
         "kernel_ms": {n: round(v, 4) for n, v in kern.items()},
+        "other_router": {"router": "bf16" if args.router_fp8 else "fp8",
+                         "route_ms": round(e0.elapsed_time(e1) / args.steps, 4),
+                         "same_expert_set_fraction": round(agree, 4)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_routing(w)
@@ -271,8 +322,9 @@ def main():
     t_wq2 = e0.elapsed_time(e1)
     del w2
     torch.cuda.empty_cache()
-    weights = moe.MoEWeights(wr, bias, w1q=w1q, w1d=w1d, w2q=w2q, w2d=w2d)
-    lay = moe.MoELayer(weights, w.T, w.k, w.gamma, device=dev)
+    weights = moe.MoEWeights(wr, bias, w1q=w1q, w1d=w1d, w2q=w2q, w2d=w2d,
+                             router_fp8=args.router_fp8)
+    lay = moe.MoELayer(weights, w.T, w.k, w.gamma, device=dev, router_fp8=args.router_fp8)
     # the batches of the workload (one for most; the skewed-load workload has
     # ten, batch b drawn with seed offset b); step i runs batch i % batches
     xs = [gen(w.x_spec(b)) for b in range(w.batches)]
@@ -282,6 +334,9 @@ def main():
     fns = [lambda: lay.route(xs[cur["i"] % len(xs)]), lay.permute,
            lambda: lay.quant_x(xs[cur["i"] % len(xs)]), lay.gemm1, lay.gemm2,
            lay.combine, lay.bias_update]
+    if args.router_fp8:    # the FP8 router reads the quantised x: quantise first
+        names = ["quant_x"] + names[:2] + names[3:]
+        fns = [fns[2]] + fns[:2] + fns[3:]
 
     def step(evs=None):
         for i, f in enumerate(fns):
@@ -354,7 +409,9 @@ def main():
     # written once) over the measured kernel time
     N, k = w.N, w.k
     phase_bytes = {
-        "route": T * H * 2 + N * H * 2 + N * 4 + T * N * 4 + T * k * 8,
+        "route": (N * H + (N // 128) * (H // 128) * 4 + T * H + T * (H // 128) * 4
+                  + N * 4 + T * N * 4 + T * k * 8) if args.router_fp8 else
+                 (T * H * 2 + N * H * 2 + N * 4 + T * N * 4 + T * k * 8),
         "quant_x": T * H * 2 + T * H + T * (H // 128) * 4,
         "combine": R * H * 2 + T * k * 8 + T * H * 2,
         "permute": T * k * 4 + N * 4 + (N + 2) * 4 + T * k * 4 + R * 4,
@@ -380,7 +437,8 @@ def main():
         "config": {"workload": f"{w.name}: T={w.T} tokens, hidden {w.H}, {w.N} routed experts "
                                f"top-{w.k} + 1 shared, SwiGLU intermediate {w.I}, FP8 E4M3 "
                                f"1x128 / 128x128 scales",
-                   "T": w.T, "H": w.H, "N": w.N, "k": w.k, "I": w.I},
+                   "T": w.T, "H": w.H, "N": w.N, "k": w.k, "I": w.I,
+                   "router": "fp8" if args.router_fp8 else "bf16"},
         "roofline": roof,
         "gemm_tflops": round(gemm_tflops, 2),
         "gemm_frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),

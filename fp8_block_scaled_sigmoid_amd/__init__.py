@@ -56,6 +56,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         sig = {
             "moe_route_topk": [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, ctypes.c_size_t, _P],
+            "moe_route_topk_fp8": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P,
+                                   ctypes.c_size_t, _P],
             "moe_topk_from_scores": [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P],
             "moe_permute": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
             "fp8_quant_1x128": [_P, _I, _I, _I, _I, _P, _P, _P],
@@ -134,6 +136,34 @@ def moe_route_topk(x, w_router, bias, k, scores=True, idx=None, gate=None, ws=No
     _check("moe_route_topk", lib().moe_route_topk(_ptr(x), _ptr(w_router), _ptr(bias), T, H, N, k,
                                                   n_groups, topk_groups, _ptr(scores), _ptr(idx),
                                                   _ptr(gate), _ptr(ws), ws.numel(), _stream(stream)))
+    return idx, gate, scores
+
+
+def moe_route_topk_fp8(x_q, x_d, w_router_q, w_router_d, bias, k, scores=True, idx=None,
+                       gate=None, ws=None, n_groups=1, topk_groups=1, stream=None):
+    """Opt-in FP8 router + biased top-k.  x_q uint8 [T,H] with x_d float32
+    [T,H/128] (fp8_quant_1x128), w_router_q uint8 [N,H] with w_router_d float32
+    [N/128,H/128] (fp8_quant_128x128), bias [N] float32.  Same outputs and
+    workspace as moe_route_topk."""
+    T, H = x_q.shape
+    N = w_router_q.shape[-2]
+    _dev(x_q, torch.uint8, "x_q"), _dev(x_d, torch.float32, "x_d")
+    _dev(w_router_q, torch.uint8, "w_router_q"), _dev(w_router_d, torch.float32, "w_router_d")
+    _dev(bias, torch.float32, "bias")
+    if scores is True:
+        scores = torch.empty(T, N, dtype=torch.float32, device=x_q.device)
+    elif scores is False:
+        scores = None
+    idx = torch.empty(T, k, dtype=torch.int32, device=x_q.device) if idx is None else idx
+    gate = torch.empty(T, k, dtype=torch.float32, device=x_q.device) if gate is None else gate
+    if ws is None:
+        ws = torch.empty(max(moe_route_workspace_bytes(T, H, N), 16), dtype=torch.uint8,
+                         device=x_q.device)
+    _check("moe_route_topk_fp8",
+           lib().moe_route_topk_fp8(_ptr(x_q), _ptr(x_d), _ptr(w_router_q), _ptr(w_router_d),
+                                    _ptr(bias), T, H, N, k, n_groups, topk_groups, _ptr(scores),
+                                    _ptr(idx), _ptr(gate), _ptr(ws), ws.numel(),
+                                    _stream(stream)))
     return idx, gate, scores
 
 
@@ -264,12 +294,17 @@ def moe_seq_balance_loss(idx, gate, seq_offsets, n_experts, alpha=1e-4, loss=Non
 class MoEWeights:
     """Device weights of one layer: router [N,H] bf16, bias [N] float32, and
     FP8 experts quantised 128x128 from bf16 W1 [G,2I,H] (gate rows, then up
-    rows) and W2 [G,H,I]; expert G-1 = N is the shared expert."""
+    rows) and W2 [G,H,I]; expert G-1 = N is the shared expert.  router_fp8
+    also keeps the router quantised 128x128 for the opt-in FP8 router."""
 
     def __init__(self, w_router, bias, w1_bf16=None, w2_bf16=None, w1q=None, w1d=None,
-                 w2q=None, w2d=None):
+                 w2q=None, w2d=None, router_fp8=False):
         self.w_router = w_router
         self.bias = bias
+        self.w_router_q = self.w_router_d = None
+        if router_fp8:   # the opt-in FP8 router: Wr quantised 128x128 as well
+            q, d = fp8_quant_128x128(w_router)
+            self.w_router_q, self.w_router_d = q[0], d[0]
         if w1_bf16 is not None:
             w1q, w1d = fp8_quant_128x128(w1_bf16, interleave_gate_up=True)
         if w2_bf16 is not None:
@@ -284,10 +319,14 @@ class MoELayer:
     """Buffers for a batch of T tokens and the forward pass over them.  All
     buffers are allocated once here; ``forward`` only enqueues kernels."""
 
-    def __init__(self, weights, T, k, gamma=1e-3, device="cuda", n_groups=1, topk_groups=1):
+    def __init__(self, weights, T, k, gamma=1e-3, device="cuda", n_groups=1, topk_groups=1,
+                 router_fp8=False):
         w = weights
         self.w, self.T, self.k, self.gamma = w, T, k, gamma
         self.n_groups, self.topk_groups = n_groups, topk_groups
+        if router_fp8 and w.w_router_q is None:
+            raise ValueError("router_fp8 needs MoEWeights(..., router_fp8=True)")
+        self.router_fp8 = router_fp8
         N, H, I = w.N, w.H, w.I
         self.with_shared = w.G == N + 1
         R = T * k + (T if self.with_shared else 0)
@@ -312,6 +351,14 @@ class MoELayer:
 
     # the individual steps, so that callers can time or replace one of them
     def route(self, x, stream=None):
+        """Routing from x (bf16 router), or from the quantised x already in
+        self.xq / self.xd (FP8 router: quant_x runs first)."""
+        if self.router_fp8:
+            moe_route_topk_fp8(self.xq, self.xd, self.w.w_router_q, self.w.w_router_d,
+                               self.w.bias, self.k, scores=self.scores, idx=self.idx,
+                               gate=self.gate, ws=self.route_ws, n_groups=self.n_groups,
+                               topk_groups=self.topk_groups, stream=stream)
+            return
         moe_route_topk(x, self.w.w_router, self.w.bias, self.k, scores=self.scores, idx=self.idx,
                        gate=self.gate, ws=self.route_ws, n_groups=self.n_groups,
                        topk_groups=self.topk_groups, stream=stream)
@@ -344,9 +391,14 @@ class MoELayer:
         """One forward pass of the layer over x [T,H] bf16; returns y [T,H]
         bf16 (a buffer of this object).  With update_bias the per-expert bias
         is updated from this batch's counts at the end."""
-        self.route(x, stream)
-        self.permute(stream)
-        self.quant_x(x, stream)
+        if self.router_fp8:
+            self.quant_x(x, stream)
+            self.route(x, stream)
+            self.permute(stream)
+        else:
+            self.route(x, stream)
+            self.permute(stream)
+            self.quant_x(x, stream)
         self.gemm1(stream)
         self.gemm2(stream)
         self.combine(stream)

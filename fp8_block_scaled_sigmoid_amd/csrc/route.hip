@@ -3,8 +3,9 @@
 // Training at 671B Scale", section III: affinity s = Sigmoid(u . e_i), chosen
 // set = TopK of s + b, gate = s normalised over the chosen set, the bias never
 // touching the gate; "DeepSeek-V3, explained.", recipe step 4).  The router
-// stays in bf16 with float accumulation, as the pages keep the gating network
-// out of FP8 (same page, section V, FP8 detail 4).
+// stays in bf16 with float accumulation by default, as the pages keep the
+// gating network out of FP8 (same page, section V, FP8 detail 4);
+// moe_route_topk_fp8 is an opt-in variant on block-scaled FP8 operands.
 //
 // moe_route_topk in two launches.  The router GEMM x [T,H] . Wr^T [H,N] is
 // split along H into S slices so that about one workgroup per compute unit
@@ -290,6 +291,150 @@ __global__ __launch_bounds__(kRThreads, 1) void route_partial_kernel(
   }
 }
 
+// The same partial logits from FP8 operands, for the opt-in FP8 router: x
+// quantised with one scale per 1x128 tile, Wr with one per 128x128 block.
+// One K chunk is one 128-wide scale block: one 16x16x128 FP8 MFMA per
+// subtile into a zero accumulator, folded into the float sum with one FMA by
+// d_x[t, c] * d_W[e / 128, c] (the block-scaled product of section V of the
+// same page, FP8 details 1-2, applied to the gating GEMM, which that section
+// otherwise keeps in higher precision: detail 4).
+typedef int i32x8_r __attribute__((ext_vector_type(8)));
+constexpr int kRStageF = (kRT + kMaxN) * 128 + kRT * 4;   // + the chunk's 128 x scales
+constexpr int kRLdsF = kRStages * kRStageF;
+
+__global__ __launch_bounds__(kRThreads, 1) void route_partial_fp8_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ xd, const uint8_t* __restrict__ wq,
+    const float* __restrict__ wd, int T, int H, int N, int S, float* __restrict__ ws) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tiles = (T + kRT - 1) / kRT;
+  const int total = tiles * S;
+  const int per_xcd = (total + 7) / 8;
+  const int slot = blockIdx.x >> 3, xcd = blockIdx.x & 7;
+  const int L = xcd * per_xcd + slot;
+  if (slot >= per_xcd || L >= total) return;
+  const int s = L / tiles, tile = L - s * tiles;
+  const int t0 = tile * kRT;
+  const int nc = H / 128;
+  const int c0 = (int)((long long)s * nc / S), c1 = (int)((long long)(s + 1) * nc / S);
+  const int nck = c1 - c0;
+
+  // row copies as in the bf16 kernel (one row = 128 codes = 128 B); waves 0
+  // and 1 also copy the chunk's x scales, 64 tokens each
+  const int chunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
+  const int lrow8 = 8 * wave + (lane >> 3);
+  const __amdgpu_buffer_rsrc_t rs_x = make_rsrc(xq, (int)((long long)T * H));
+  const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(wq, N * H);
+  const __amdgpu_buffer_rsrc_t rs_d = make_rsrc(xd, T * nc * 4);
+  int x_off[2], w_off[4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int t = min(t0 + 64 * j + lrow8, T - 1);
+    x_off[j] = t * H + chunk * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = min(64 * j + lrow8, N - 1);
+    w_off[j] = e * H + chunk * 16;
+  }
+  const int d_off = min(t0 + 64 * (wave & 1) + lane, T - 1) * nc * 4;
+  auto issue = [&](int i, uint8_t* st) {
+    const int ko = (c0 + i) * 128;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_x, (lds_ptr_t)(st + (8 * j + wave) * 1024), 16,
+                                               x_off[j], ko, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs_w, (lds_ptr_t)(st + kRT * 128 + (8 * j + wave) * 1024), 16, w_off[j], ko, 0, 0);
+    if (wave < 2)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs_d, (lds_ptr_t)(st + (kRT + kMaxN) * 128 + wave * 256), 4, d_off, (c0 + i) * 4, 0, 0);
+  };
+
+  // wave tile and fragments as in the bf16 kernel; a lane's 32 codes of a
+  // row are 16-byte chunks lk and lk + 4 (the same K order for x and Wr)
+  const int wm = wave & 1, wn = wave >> 1;
+  const int lrow = lane & 15, lk = lane >> 4;
+  const int ni_valid = clampi_dev((N - wn * 64) >> 4, 0, 4);
+  const int sw = (lrow >> 1) & 7;
+  const int frag_lo = lrow * 128 + ((lk ^ sw) << 4);
+  const int frag_hi = lrow * 128 + (((lk + 4) ^ sw) << 4);
+  const float* wd_row = wd + (long long)((wn * 64) >> 7) * nc;   // the wave's 64 experts share a block
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto kloop = [&](auto ni_c) {
+    constexpr int NI = decltype(ni_c)::value;
+    issue(0, smem);
+    if (nck > 1) issue(1, smem + kRStageF);
+    for (int i = 0; i < nck; ++i) {
+      if (i + 1 < nck) {
+        if (wave < 2) wait_and_barrier<7>();
+        else wait_and_barrier<6>();
+      } else {
+        wait_and_barrier<0>();
+      }
+      if (i + 2 < nck) issue(i + 2, smem + ((i + 2) % kRStages) * kRStageF);
+      if (NI == 0) continue;
+      const uint8_t* st = smem + (i % kRStages) * kRStageF;
+      const float* sx = reinterpret_cast<const float*>(st + (kRT + kMaxN) * 128) + wm * 64 + 4 * lk;
+      const float sw_blk = wd_row[c0 + i];
+      i32x8_r af[4], bfr[NI > 0 ? NI : 1];
+      f32x4 sc[4];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const uint8_t* a = st + (wm * 64 + mi * 16) * 128;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(a + frag_lo);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(a + frag_hi);
+        af[mi] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        sc[mi] = *reinterpret_cast<const f32x4*>(sx + mi * 16) * sw_blk;
+      }
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const uint8_t* b = st + (kRT + wn * 64 + ni * 16) * 128;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(b + frag_lo);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(b + frag_hi);
+        bfr[ni] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af[mi], bfr[ni], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            acc[mi][ni][v] = __builtin_fmaf(part[v], sc[mi][v], acc[mi][ni][v]);
+        }
+    }
+    if (NI == 0) return;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = t0 + wm * 64 + mi * 16 + 4 * lk + v;
+        if (t < T) {
+          float* row = ws + ((long long)s * T + t) * N + wn * 64 + lrow;
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) row[ni * 16] = acc[mi][ni][v];
+        }
+      }
+  };
+  switch (__builtin_amdgcn_readfirstlane(ni_valid)) {
+    case 4: kloop(std::integral_constant<int, 4>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    default: kloop(std::integral_constant<int, 0>{}); break;
+  }
+}
+
 // One wave per token: logits = sum of the S partials in slice order, scores =
 // sigmoid, then the biased top k and the unbiased gates.
 template <int PER>
@@ -397,6 +542,53 @@ extern "C" moe_status_t moe_route_topk(const void* x_bf16, const void* w_router_
   hipLaunchKernelGGL(route_partial_kernel, dim3(grid), dim3(kRThreads), kRLds, stream,
                      static_cast<const uint16_t*>(x_bf16),
                      static_cast<const uint16_t*>(w_router_bf16), T, H, N, S, part);
+  if (moe_status_t st = launch_status()) return st;
+  const int blocks = (T + 3) / 4;
+  const int per = (N + 63) / 64;
+#define MOE_FINISH_LAUNCH(P)                                                                  \
+  hipLaunchKernelGGL(route_finish_kernel<P>, dim3(blocks), dim3(256), 0, stream, part, S, bias, \
+                     T, N, k, n_groups, topk_groups, scores, topk_idx, topk_gate)
+  if (per <= 1) MOE_FINISH_LAUNCH(1);
+  else if (per <= 2) MOE_FINISH_LAUNCH(2);
+  else MOE_FINISH_LAUNCH(4);
+#undef MOE_FINISH_LAUNCH
+  return launch_status();
+}
+
+extern "C" moe_status_t moe_route_topk_fp8(const uint8_t* x_q, const float* x_d,
+                                           const uint8_t* w_router_q, const float* w_router_d,
+                                           const float* bias, int T, int H, int N, int k,
+                                           int n_groups, int topk_groups, float* scores,
+                                           int32_t* topk_idx, float* topk_gate, void* ws,
+                                           size_t ws_bytes, hipStream_t stream) {
+  if (T < 0 || H < 0 || H % 128 != 0 || N < 128 || N > kMaxN || N % 128 != 0 || k < 1 ||
+      k > 32 || k > N || !groups_ok(N, k, n_groups, topk_groups))
+    return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (H == 0) return MOE_ERR_SHAPE;
+  // in-kernel byte offsets are 32-bit
+  if ((long long)T * H >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!x_q || !x_d || !w_router_q || !w_router_d || !bias || !topk_idx || !topk_gate)
+    return MOE_ERR_NULL;
+  // this path splits H at most as finely as the bf16 one, so the bf16 size bounds it
+  if (!ws || ws_bytes < moe_route_workspace_bytes(T, H, N)) return MOE_ERR_WORKSPACE;
+  if (!aligned16(x_q) || !aligned16(w_router_q) || !aligned16(ws) ||
+      (reinterpret_cast<uintptr_t>(x_d) & 3) || (reinterpret_cast<uintptr_t>(w_router_d) & 3))
+    return MOE_ERR_ALIGN;
+  if (moe_status_t st = check_device()) return st;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_partial_fp8_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kRLdsF);
+    if (e != hipSuccess) return hip_fail(e);
+    attr_set = true;
+  }
+  const int S = route_splits(T, H / 2);   // one chunk here is 128 codes, not 64
+  const int tiles = (T + kRT - 1) / kRT;
+  const int grid = (tiles * S + 7) / 8 * 8;
+  float* part = static_cast<float*>(ws);
+  hipLaunchKernelGGL(route_partial_fp8_kernel, dim3(grid), dim3(kRThreads), kRLdsF, stream, x_q,
+                     x_d, w_router_q, w_router_d, T, H, N, S, part);
   if (moe_status_t st = launch_status()) return st;
   const int blocks = (T + 3) / 4;
   const int per = (N + 63) / 64;

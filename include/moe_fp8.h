@@ -94,6 +94,28 @@ moe_status_t moe_route_topk(const void* x_bf16, const void* w_router_bf16, const
                             size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Opt-in FP8 router: the same scores, selection and gates as moe_route_topk,
+ * but the logits come from block-scaled FP8 operands (the product of [TP]
+ * section V, FP8 details 1-2, applied to the gating GEMM, which detail 4
+ * keeps in higher precision; hence opt-in, and its routing can differ from
+ * the bf16 router's on tokens whose k-th and (k+1)-th keys are close):
+ *   z[t,i] = sum_c d_x[t,c] * d_W[i/128,c] * sum_{h in block c} q_x[t,h] q_W[i,h]
+ * x_q E4M3 [T,H] with x_d float [T,H/128] (fp8_quant_1x128 output);
+ * w_router_q E4M3 [N,H] with w_router_d float [N/128,H/128]
+ * (fp8_quant_128x128 output).  Each block product is formed by the MFMA in
+ * float and scaled with one FMA; blocks are added in order within an H slice
+ * and the slices in slice order.  ws as for moe_route_topk (the same size
+ * suffices).  Requires H % 128 == 0, N % 128 == 0, 128 <= N <= 256,
+ * 1 <= k <= min(N, 32), T * H < 2^31 (MOE_ERR_UNSUPPORTED otherwise); x_q,
+ * w_router_q and ws 16-byte aligned, the scale arrays 4-byte aligned.
+ */
+moe_status_t moe_route_topk_fp8(const uint8_t* x_q, const float* x_d, const uint8_t* w_router_q,
+                                const float* w_router_d, const float* bias, int T, int H, int N,
+                                int k, int n_groups, int topk_groups, float* scores,
+                                int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/*
  * The selection and gate steps alone, from a given float score tensor
  * scores [T,N] (same definitions as moe_route_topk, group-limited selection
  * included).  Requires 1 <= N <= 1024, 1 <= k <= min(N, 32).

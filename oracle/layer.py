@@ -36,17 +36,21 @@ def expert_rows(xq, xd, tokens, wq, g, precision="D"):
 
 
 def moe_layer(x, w_r, bias, w1, w2, k, gamma, precision="D", idx=None, wq=None, n_groups=1,
-              topk_groups=1):
+              topk_groups=1, router_fp8=False):
     """x [T, H], w_r [N, H], bias [N] float32, w1 [N+1, 2I, H],
     w2 [N+1, H, I] (expert N is the shared one).  ``idx`` overrides the
     oracle's own routing (to line it up with a routing decided elsewhere);
     ``wq`` supplies already-quantised weights; n_groups > 1 selects with the
-    group-limited rule (``route.select_topk_grouped``).  Returns a dict of
+    group-limited rule (``route.select_topk_grouped``); router_fp8 scores
+    with the opt-in FP8 router (``route.route_fp8``).  Returns a dict of
     every intermediate."""
     x = np.asarray(x, np.float64)
     T, H = x.shape
     N = w_r.shape[0]
-    s64, s32, idx_o, gate_o = _route.route(x, w_r, bias, k)
+    if router_fp8:
+        s64, s32, idx_o, gate_o, _ = _route.route_fp8(x, w_r, bias, k)
+    else:
+        s64, s32, idx_o, gate_o = _route.route(x, w_r, bias, k)
     if n_groups > 1:
         idx_o = _route.select_topk_grouped(s32, bias, k, n_groups, topk_groups)
         gate_o = _route.gates(s32, idx_o)

@@ -23,6 +23,13 @@ loss", last sentences; [TP] section V, "Custom all-to-all kernels"): the N
 experts are split into G equal groups of consecutive indices (one group per
 node); a group's score is the sum of its K_r / M highest keys; only the M best
 groups are eligible, and the K_r experts are the best keys among them.
+Opt-in FP8 router.  The pages keep the gating network in BF16/FP32 ([TP]
+section V, FP8 detail 4; [VE] recipe step 7); the FP8 option applies the
+block-scaled product of [TP] section V (details 1-2, Figure 6) to the router:
+x quantised 1x128, W_r quantised 128x128 (its rows are the experts), and
+  z[t, i] = sum_c d_x[t, c] d_W[i / 128, c] sum_{h in block c} q_x[t, h] q_W[i, h]
+in float64; scores, selection and gates then follow as above.
+
 Readings where the pages leave a step open:
   * the keys are the biased keys (selection, including the group ranking, is
     where the bias acts; the gates stay unbiased);
@@ -31,6 +38,9 @@ Readings where the pages leave a step open:
   * groups are ranked by (score descending, group index ascending).
 """
 import numpy as np
+
+from . import ffn as _ffn
+from . import quant as _quant
 
 
 def router_logits(x, w_r):
@@ -47,6 +57,25 @@ def sigmoid(z):
     ez = np.exp(z[~pos])
     out[~pos] = ez / (1.0 + ez)
     return out
+
+
+def router_logits_fp8(xq, xd, wq, wd):
+    """z [T, N] float64 from quantised operands: x codes [T, H] with 1x128
+    scales [T, H/128], W_r codes [N, H] with 128x128 scales [N/128, H/128]."""
+    return _ffn.block_scaled_gemm(xq, xd, wq, wd)
+
+
+def route_fp8(x, w_r, bias, k, n_groups=1, topk_groups=1):
+    """Routing through the opt-in FP8 router: x and W_r quantised by the
+    oracle's own quantisers, logits from the block-scaled product, then the
+    same sigmoid, selection and gates as ``route``.  Returns
+    (s64, s32, idx, gate, (xq, xd, wq, wd))."""
+    xq, xd = _quant.quant_1x128(x)
+    wq, wd = _quant.quant_128x128(w_r)
+    s64 = sigmoid(router_logits_fp8(xq, xd, wq, wd))
+    s32 = s64.astype(np.float32)
+    idx = select_topk_grouped(s32, bias, k, n_groups, topk_groups)
+    return s64, s32, idx, gates(s32, idx), (xq, xd, wq, wd)
 
 
 def router_scores(x, w_r):

@@ -29,7 +29,8 @@ def lib():
 
 def test_header_declares_the_layer_calls():
     names = declared_functions()
-    for n in ["moe_route_topk", "moe_route_workspace_bytes", "moe_topk_from_scores", "moe_permute",
+    for n in ["moe_route_topk", "moe_route_topk_fp8", "moe_route_workspace_bytes",
+              "moe_topk_from_scores", "moe_permute",
               "moe_permute_workspace_bytes", "fp8_quant_1x128", "fp8_quant_128x128",
               "moe_grouped_gemm_fp8", "moe_combine", "moe_bias_update", "moe_status_str",
               "moe_last_hip_error"]:
@@ -79,6 +80,17 @@ def test_validation_before_any_launch(lib):
     # missing workspace (checked before any device access)
     assert R(4, 256, 16, 2, x=dummy) == 4
     assert R(4, 256, 256, 8, 8, 4, x=dummy) == 4
+    lib.moe_route_topk_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, P, P,
+                                       ctypes.c_size_t, P]
+    R8 = lambda T, H, N, k, G=1, M=1, x=None, ws=None: lib.moe_route_topk_fp8(  # noqa: E731
+        x, x, x, x, x, T, H, N, k, G, M, None, x, x, ws, 0, None)
+    assert R8(4, 256, 16, 2) == 2                 # N below one 128-row weight block
+    assert R8(4, 256, 192, 8) == 2                # N % 128
+    assert R8(4, 200, 256, 8) == 2                # H % 128
+    assert R8(4, 256, 256, 8, 8, 3) == 2
+    assert R8(0, 256, 256, 8) == 0
+    assert R8(4, 256, 256, 8) == 1                # NULL operands
+    assert R8(4, 256, 256, 8, x=dummy) == 4       # missing workspace
     lib.moe_topk_from_scores.argtypes = [P, P, I, I, I, I, I, P, P, P]
     assert lib.moe_topk_from_scores(None, None, 4, 256, 8, 8, 3, None, None, None) == 2
     assert lib.moe_topk_from_scores(None, None, 0, 256, 8, 8, 4, None, None, None) == 0

@@ -247,6 +247,104 @@ def test_route_topk_full_routing_workload_sampled():
                  gate.cpu().numpy()[rows])
 
 
+# --------------------------------------------------------------------------- FP8 router
+
+
+FP8_ROUTER_REL = 1e-4   # |logit - exact block-scaled sum| / sum|q_x q_W d_x d_W|, as for the GEMM
+
+
+def _route_fp8_check(xb, wrb, b, k, xq, xd, wq, wd, s_gpu, idx_gpu, gate_gpu, idx_bf16,
+                     G=1, M=1):
+    """The opt-in FP8 router against the oracle's FP8 router: operand codes
+    and scales bit-exact to the oracle's quantisers; selection bit-exact to
+    the rule on the GPU's own scores; scores within the MFMA band of the
+    float64 block-scaled product; index sets equal to the oracle's wherever
+    the key gap exceeds twice that band.  Returns the fraction of tokens
+    routed to the same set as the bf16 router."""
+    xq_o, xd_o = quant.quant_1x128(synth.as_f64(xb))
+    wq_o, wd_o = quant.quant_128x128(synth.as_f64(wrb))
+    assert np.array_equal(xq, xq_o) and np.array_equal(xd, xd_o)
+    assert np.array_equal(wq, wq_o) and np.array_equal(wd, wd_o)
+    assert np.array_equal(idx_gpu, route.select_topk_grouped(s_gpu, b, k, G, M))
+    np.testing.assert_allclose(gate_gpu, route.gates(s_gpu, idx_gpu), rtol=2e-6, atol=1e-7)
+    s64 = route.sigmoid(route.router_logits_fp8(xq_o, xd_o, wq_o, wd_o))
+    mag = route.router_logits_fp8(xq_o & 0x7F, xd_o, wq_o & 0x7F, wd_o)
+    tol = 0.25 * FP8_ROUTER_REL * mag + 2e-7          # sigmoid' <= 1/4, plus float32 rounding
+    err = np.abs(s_gpu - s64)
+    print(f"max |score - oracle| = {err.max():.3e} (bound {tol.max():.3e}, "
+          f"max ratio {np.max(err / tol):.3f})")
+    assert np.all(err <= tol)
+    if G <= 1:
+        margin = route.topk_margin(s64, b, k)
+        clear = margin > 2 * (tol.max(axis=1) + 1e-7)
+        want = route.select_topk(s64.astype(np.float32), b, k)
+        print(f"tokens with a clear margin: {clear.mean():.3f}")
+        assert np.array_equal(np.sort(idx_gpu[clear], 1), np.sort(want[clear], 1))
+    agree = float(np.mean(np.all(np.sort(idx_gpu, 1) == np.sort(idx_bf16, 1), axis=1)))
+    print(f"agreement with the bf16 router (same expert set): {agree:.4f}")
+    return agree
+
+
+def _run_route_fp8(moe, x_dev, wr_dev, b, k, G=1, M=1):
+    xq, xd = moe.fp8_quant_1x128(x_dev)
+    wq, wd = moe.fp8_quant_128x128(wr_dev)
+    idx, gate, s = moe.moe_route_topk_fp8(xq, xd, wq[0], wd[0], to_dev(b), k, n_groups=G,
+                                          topk_groups=M)
+    idx_b, _, _ = moe.moe_route_topk(x_dev, wr_dev, to_dev(b), k, scores=False, n_groups=G,
+                                     topk_groups=M)
+    torch.cuda.synchronize()
+    return (xq.cpu().numpy(), xd.cpu().numpy(), wq[0].cpu().numpy(), wd[0].cpu().numpy(),
+            s.cpu().numpy(), idx.cpu().numpy(), gate.cpu().numpy(), idx_b.cpu().numpy())
+
+
+@pytest.mark.parametrize("name,T,G,M", [("routing", 2048, 1, 1), ("prefill", 1000, 1, 1),
+                                        ("skew", 512, 1, 1), ("routing", 777, 8, 4)])
+def test_route_topk_fp8(name, T, G, M):
+    moe = _moe()
+    w = synth.WORKLOADS[name]
+    xb = synth.generate(w.x_spec(), w.seed, rows=np.arange(T))
+    wrb = w.router_weight()
+    b = w.bias()
+    log(f"moe_route_topk_fp8 {name} T={T} G={G} M={M}")
+    r = _run_route_fp8(moe, bf16_to_dev(xb), bf16_to_dev(wrb), b, w.k, G, M)
+    agree = _route_fp8_check(xb, wrb, b, w.k, *r, G=G, M=M)
+    assert agree > 0.5
+
+
+def test_route_topk_fp8_ragged_small():
+    """T off the 128-token tile, one and two 128-expert blocks, one H block,
+    k = 1 and k = 32 (the largest)."""
+    moe = _moe()
+    rng = np.random.default_rng(6)
+    for T, H, N, k in [(33, 256, 128, 4), (129, 640, 256, 8), (300, 1024, 128, 8),
+                       (1, 128, 128, 1), (70, 384, 128, 128 // 4)]:
+        x = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+        wr = synth.f32_to_bf16_bits((rng.standard_normal((N, H)) * 0.05).astype(np.float32))
+        b = rng.uniform(-0.1, 0.1, N).astype(np.float32)
+        log(f"moe_route_topk_fp8 ragged T={T} H={H} N={N} k={k}")
+        r = _run_route_fp8(moe, bf16_to_dev(x), bf16_to_dev(wr), b, k)
+        _route_fp8_check(x, wr, b, k, *r)
+
+
+def test_route_topk_fp8_full_routing_workload_sampled():
+    """The routing workload at full size (T = 16384) through the FP8 router;
+    the oracle checks a seeded sample of 256 tokens (first, last, random)."""
+    moe = _moe()
+    w = synth.WORKLOADS["routing"]
+    x = device_tensor(w.x_spec(), w.seed)
+    wrb = w.router_weight()
+    b = w.bias()
+    log(f"moe_route_topk_fp8 routing full T={w.T}")
+    xq, xd, wq, wd, s, idx, gate, idx_b = _run_route_fp8(moe, x, bf16_to_dev(wrb), b, w.k)
+    rng = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([[0, 1, w.T - 1], rng.choice(w.T, 253, replace=False)]))
+    xb = synth.generate(w.x_spec(), w.seed, rows=rows)
+    _route_fp8_check(xb, wrb, b, w.k, xq[rows], xd[rows], wq, wd, s[rows], idx[rows], gate[rows],
+                     idx_b[rows])
+    agree = float(np.mean(np.all(np.sort(idx, 1) == np.sort(idx_b, 1), axis=1)))
+    print(f"agreement with the bf16 router over all {w.T} tokens: {agree:.4f}")
+
+
 @pytest.mark.parametrize("T,N,G,M,k,ties", [(1000, 256, 8, 4, 8, False), (777, 256, 8, 4, 8, True),
                                             (300, 64, 4, 2, 4, False), (200, 960, 60, 6, 12, True),
                                             (64, 16, 2, 1, 2, False), (50, 48, 3, 3, 3, True)])

@@ -153,6 +153,47 @@ def test_layer_tiny_group_limited():
     assert agree.mean() > 0.95
 
 
+def test_layer_fp8_router():
+    """A small layer with the opt-in FP8 router (128 experts top-4): routing on
+    the GPU's own scores is the selection rule bit for bit, the scores sit in
+    the FP8 router's band around the oracle's FP8 router, and the rest of the
+    layer matches the oracle given that routing."""
+    moe = _moe()
+    w = synth.Workload("fp8r", T=300, H=512, N=128, k=4, I=256, x_std=1.0, wr_dist=synth.NORMAL,
+                       wr_param=0.05, bias_half=0.1, w_std=0.02, seed=7)
+    x_b = synth.generate(w.x_spec(), w.seed)
+    wr_b = w.router_weight()
+    w1_b = synth.generate(w.w1_spec(), w.seed)
+    w2_b = synth.generate(w.w2_spec(), w.seed)
+    b = w.bias()
+    log("layer fp8 router T=300 H=512 N=128 k=4")
+    weights = moe.MoEWeights(bf16_to_dev(wr_b), to_dev(b.copy()), w1_bf16=bf16_to_dev(w1_b),
+                             w2_bf16=bf16_to_dev(w2_b), router_fp8=True)
+    lay = moe.MoELayer(weights, w.T, w.k, w.gamma, router_fp8=True)
+    y = bf16_values(lay.forward(bf16_to_dev(x_b)))
+    torch.cuda.synchronize()
+    args = (synth.as_f64(x_b), synth.as_f64(wr_b), b, synth.as_f64(w1_b), synth.as_f64(w2_b),
+            w.k, w.gamma)
+    s_gpu = lay.scores.cpu().numpy()
+    idx = lay.idx.cpu().numpy()
+    assert np.array_equal(idx, route.select_topk(s_gpu, b, w.k))
+    q = olayer.moe_layer(*args, precision="Q", idx=idx, router_fp8=True)
+    xq, xd, wq, wd = route.route_fp8(args[0], args[1], b, w.k)[4]
+    mag = route.router_logits_fp8(xq & 0x7F, xd, wq & 0x7F, wd)   # sum |d_x d_W q_x q_W|
+    assert np.all(np.abs(s_gpu - q["s64"]) <= 0.25e-4 * mag + 2e-7)
+    np.testing.assert_allclose(lay.gate.cpu().numpy(), q["gate"], rtol=1e-4, atol=1e-6)
+    assert np.array_equal(lay.xq.cpu().numpy(), q["xq"])
+    assert np.array_equal(lay.counts.cpu().numpy(), q["counts"])
+    assert np.array_equal(lay.row_of.cpu().numpy(), q["row_of"])
+    assert np.array_equal(weights.bias.cpu().numpy(), q["bias"])
+    err_q = rel_l2(y, q["y"])
+    d = olayer.moe_layer(*args, precision="D", idx=idx, router_fp8=True)
+    err_d = max_rel(y, d["y"])
+    print(f"rel L2 vs Q = {err_q:.3e}, normwise max rel vs D = {err_d:.3e}")
+    assert err_q <= E2E_Q_BAR
+    assert err_d <= D_BAR
+
+
 def test_layer_zero_input():
     w = synth.WORKLOADS["tiny"]
     zero = np.zeros((w.T, w.H), np.uint16)

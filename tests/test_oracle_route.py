@@ -229,3 +229,89 @@ def test_grouped_topk_limits_the_groups_and_keeps_gates_unbiased():
     b3[32 * 7 + 5] = 2.0
     idx3 = route.select_topk_grouped(s, b3, k, G, M)[0]
     assert 32 * 7 + 5 in idx3 and 7 in {e // 32 for e in idx3}
+
+
+# --------------------------------------------------------------------------- opt-in FP8 router
+# "DeepSeek-V3: Auxiliary-Loss-Free MoE Load Balancing, Multi-Token Prediction,
+# and FP8 Training at 671B Scale", section V, FP8 details 1-2 (1x128 activation
+# tiles, 128x128 weight blocks) applied to the router's product.
+
+from oracle import e4m3  # noqa: E402
+
+
+def _e4m3_tiles(rng, rows, cols, exps, block_rows):
+    """Values that E4M3 holds exactly once divided by their block's power of
+    two: random finite codes, one +448 per block (so amax = 448 * 2^p and the
+    quantiser's scale is exactly 2^p), block (r // block_rows, c // 128)
+    scaled by 2^exps[r // block_rows, c // 128]."""
+    codes = rng.integers(0, 256, (rows, cols)).astype(np.uint8)
+    codes = np.where((codes & 0x7F) == 0x7F, codes & 0xF0, codes).astype(np.uint8)
+    v = e4m3.decode(codes)
+    for rb in range(rows // block_rows):
+        for cb in range(cols // 128):
+            v[rb * block_rows, cb * 128] = 448.0
+    scale = np.repeat(np.repeat(2.0 ** np.asarray(exps, np.float64), block_rows, 0), 128, 1)
+    return v * scale
+
+
+def test_fp8_router_is_exact_on_e4m3_operands():
+    """Operands that the quantisers reproduce exactly: the FP8 logits equal the
+    plain float64 product, and the routing equals the bf16-free oracle's."""
+    rng = np.random.default_rng(21)
+    T, H, N, k = 40, 512, 256, 8
+    x = _e4m3_tiles(rng, T, H, rng.integers(-9, -3, (T, H // 128)), 1)
+    w = _e4m3_tiles(rng, N, H, np.array([[-14, -13, -12, -11], [-12, -15, -11, -13]]), 128)
+    b = rng.uniform(-0.05, 0.05, N).astype(np.float32)
+    s64f, s32f, idxf, gatef, (xq, xd, wq, wd) = route.route_fp8(x, w, b, k)
+    np.testing.assert_array_equal(e4m3.decode(xq) * np.repeat(xd.astype(np.float64), 128, 1), x)
+    z = route.router_logits(x, w)
+    zf = route.router_logits_fp8(xq, xd, wq, wd)
+    scale = np.abs(x) @ np.abs(w).T
+    assert np.max(np.abs(zf - z) / scale) < 1e-13
+    s64, s32, idx, gate = route.route(x, w, b, k)
+    clear = route.topk_margin(s64, b, k) > 1e-9
+    assert clear.mean() > 0.99
+    assert np.array_equal(idxf[clear], idx[clear])
+
+
+def test_fp8_router_dequantised_dot_brute_force():
+    """The block-scaled sum equals the dot product of the dequantised operands,
+    written out element by element (tiny case, two weight block rows)."""
+    rng = np.random.default_rng(22)
+    T, H, N = 2, 256, 256
+    x = rng.standard_normal((T, H)) * np.repeat([[1.0, 30.0]], T, 0).repeat(128, 1)
+    w = rng.standard_normal((N, H)) * 0.02
+    w[128:] *= 7.0
+    _, _, _, _, (xq, xd, wq, wd) = route.route_fp8(x, w, np.zeros(N, np.float32), 2)
+    zf = route.router_logits_fp8(xq, xd, wq, wd)
+    xv, wv = e4m3.decode(xq), e4m3.decode(wq)
+    for t in range(T):
+        for i in range(0, N, 37):
+            acc = 0.0
+            for h in range(H):
+                acc += (xv[t, h] * float(xd[t, h // 128])) * (wv[i, h] * float(wd[i // 128, h // 128]))
+            assert abs(zf[t, i] - acc) <= 1e-12 * (abs(acc) + 1.0)
+
+
+def test_fp8_router_within_the_e4m3_error_bound():
+    """Random operands with tile- and block-dependent magnitudes: the FP8
+    logits differ from the exact product by no more than the E4M3 rounding
+    allows (relative 2^-4 on normal codes, 2^-10 of the scale below them),
+    with the scales computed here from each block's amax."""
+    rng = np.random.default_rng(23)
+    T, H, N = 64, 768, 256
+    x = rng.standard_normal((T, H)) * np.exp2(rng.integers(-6, 6, (T, H // 128))).repeat(128, 1)
+    x[:, 5] *= 100.0                                    # an outlier channel
+    wexp = rng.integers(-9, -3, (N // 128, H // 128))
+    w = rng.standard_normal((N, H)) * np.exp2(wexp).repeat(128, 0).repeat(128, 1)
+    _, _, _, _, (xq, xd, wq, wd) = route.route_fp8(x, w, np.zeros(N, np.float32), 8)
+    zf = route.router_logits_fp8(xq, xd, wq, wd)
+    z = route.router_logits(x, w)
+    dx = np.abs(x).reshape(T, H // 128, 128).max(2) / 448.0
+    dw = np.abs(w).reshape(N // 128, 128, H // 128, 128).max((1, 3)) / 448.0
+    ex = np.abs(x) * (2.0 ** -4 + 2.0 ** -20) + dx.repeat(128, 1) * 2.0 ** -10 * (1 + 1e-6)
+    ew = np.abs(w) * (2.0 ** -4 + 2.0 ** -20) + dw.repeat(128, 0).repeat(128, 1) * 2.0 ** -10 * (1 + 1e-6)
+    bound = ex @ np.abs(w).T + (np.abs(x) + ex) @ ew.T
+    ratio = np.abs(zf - z) / bound
+    assert np.max(ratio) <= 1.0
+    assert np.max(ratio) > 1e-3          # the error is real: the check is not vacuous
