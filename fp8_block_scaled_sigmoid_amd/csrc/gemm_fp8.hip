@@ -112,6 +112,16 @@ __device__ __forceinline__ void wait_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Maximum over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15): swap
+// neighbours, swap pairs, mirror the 8-lane halves, mirror the row.
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -247,6 +257,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
       dma4(rs_sa, sa_off, kb * 4, st + kABytes + kBBytes + wave * 256);
     }
   };
+  // copy i (0-5) of this wave's A and B share of a stage: A loads 0-1, B loads 0-3
+  auto issue_one = [&](int kb, uint8_t* st, int i) {
+    const int ko = kb * BK;
+    if (i < 2) dma16(rs_a, a_off[i], ko, st + (8 * i + wave) * 1024);
+    else dma16(rs_b, b_off[i - 2], ko, st + kABytes + (8 * (i - 2) + wave) * 1024);
+  };
   auto issue = [&](int kb, uint8_t* st) {
 #pragma unroll
     for (int part = 0; part < 4; ++part) issue_part(kb, st, part);
@@ -271,90 +287,192 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 
   // The K loop, for a wave whose first NMI 16-row subtiles hold valid rows
   // (the others are padding of a group's last row tile and skip their MFMAs).
+  //
+  // Two wave groups take turns ("ping-pong"): waves 0-3 and waves 4-7 each
+  // hold one wave per SIMD.  Every K block kb has two phases separated by
+  // workgroup barriers; in each phase one group issues the 16 MFMAs of its
+  // K block while the other, on the same SIMDs, runs the VALU and memory work:
+  // the scale FMAs of its previous MFMAs, its share of the copies of a later
+  // stage, and the LDS reads of its next fragments.  So the MFMA pipe and the
+  // VALU / LDS / TA paths of every SIMD are busy at the same time.
+  //   phase E_kb: group 0 MFMAs of kb;  group 1 FMAs of kb-1, copies of stage
+  //               kb+2, reads of kb;  then every wave waits for its copies of
+  //               stage kb+1 and its LDS reads;
+  //   phase O_kb: group 1 MFMAs of kb;  group 0 FMAs of kb, copies of stage
+  //               kb+3, reads of kb+1.
+  // Stage kb (ring slot kb % 3) is read by group 0 in O_kb-1 and by group 1
+  // in E_kb, so its slot is free from O_kb on.
   auto kloop = [&](auto nmi_c) {
     constexpr int NMI = decltype(nmi_c)::value;
-    // one K block.  MORE: stage kb + 2 exists and is requested meanwhile;
-    // LAST: no stage follows this one.
-    auto kblock = [&](int kb, auto more_c, auto last_c) {
-      constexpr bool more = decltype(more_c)::value, last = decltype(last_c)::value;
-      // stage kb must have landed; stage kb + 1 may still be in flight
-      if (!last) {
-        if (wave < 2) wait_and_barrier<7>(); else wait_and_barrier<6>();
-      } else {
-        wait_and_barrier<0>();
-      }
-      uint8_t* st_next = smem + ((kb + 2) % kStages) * kStage;
-      if (NMI == 0) {
-        if (more) issue(kb + 2, st_next);
-        return;
-      }
-      // MFMA lane group lk takes the 16-byte K chunks lk and lk + 4 of its
-      // row, for A and B alike (a fixed permutation of K inside the block,
-      // so the dot product is unchanged); this keeps each ds_read_b128 free
-      // of LDS bank conflicts, which chunks 2 lk and 2 lk + 1 are not.
-      // The A fragments, row scales and the first B fragment are read first;
-      // then for each column subtile ni: the next B fragment is read and one
-      // part of stage kb + 2 is requested while the 4 MFMAs of ni run, with
-      // the scale FMAs of subtile ni - 1 behind them (no FMA waits on a
-      // fresh result).
-      // Subtile rows differ by multiples of 16, so a lane's swizzle term is
-      // the same in every subtile: one lane offset per chunk half, and the
-      // subtiles sit at constant offsets from it.
+    const bool g1 = wave >= 4;
+    const int n_w = wave < 2 ? 7 : 6;          // copies per stage of this wave
+    i32x8 af[4], bfr[4];
+    f32x4 part[4][4], sc[4];
+    // MFMA lane group lk takes the 16-byte K chunks lk and lk + 4 of its row,
+    // for A and B alike (a fixed permutation of K inside the block, so the
+    // dot product is unchanged); this keeps each ds_read_b128 free of LDS bank
+    // conflicts, which chunks 2 lk and 2 lk + 1 are not.  Subtile rows differ
+    // by multiples of 16, so a lane's swizzle term is the same in every
+    // subtile: one lane offset per chunk half.
+    auto read_frags = [&](int kb) {
       const uint8_t* st = smem + (kb % kStages) * kStage;
-      const float* sA = reinterpret_cast<const float*>(st + kABytes + kBBytes) + wm * 64 + 4 * lk;
-      const float sb = s_bd[wn >> 1][kb];
       const uint8_t* a_lo = st + wm * 64 * 128 + frag_lo;
       const uint8_t* a_hi = st + wm * 64 * 128 + frag_hi;
       const uint8_t* b_lo = st + kABytes + wn * 64 * 128 + frag_lo;
       const uint8_t* b_hi = st + kABytes + wn * 64 * 128 + frag_hi;
-      auto read_b = [&](int ni) {
-        const i32x4 y0 = *reinterpret_cast<const i32x4*>(b_lo + ni * 16 * 128);
-        const i32x4 y1 = *reinterpret_cast<const i32x4*>(b_hi + ni * 16 * 128);
-        return __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
-      };
-      // read order = use order: A0 and B0 first, so the first MFMA waits for
-      // four reads only, then the other A fragments, then the row scales
-      // (first needed by the FMAs behind the second column subtile)
-      f32x4 sc[4];
-      i32x8 af[4], bfr[2];
-      auto read_a = [&](int mi) {
+#pragma unroll
+      for (int mi = 0; mi < NMI; ++mi) {
         const i32x4 x0 = *reinterpret_cast<const i32x4*>(a_lo + mi * 16 * 128);
         const i32x4 x1 = *reinterpret_cast<const i32x4*>(a_hi + mi * 16 * 128);
-        return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-      };
-      af[0] = read_a(0);
-      bfr[0] = read_b(0);
+        af[mi] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
 #pragma unroll
-      for (int mi = 1; mi < NMI; ++mi) af[mi] = read_a(mi);
-#pragma unroll
-      for (int mi = 0; mi < NMI; ++mi) sc[mi] = *reinterpret_cast<const f32x4*>(sA + mi * 16);
-#pragma unroll
-      for (int mi = 0; mi < NMI; ++mi) sc[mi] = sc[mi] * sb;
-      f32x4 part[2][4];
-#pragma unroll
-      for (int ni = 0; ni < 5; ++ni) {
-        if (ni < 3) bfr[(ni + 1) & 1] = read_b(ni + 1);
-        if (ni < 4 && more) issue_part(kb + 2, st_next, ni);
-#pragma unroll
-        for (int mi = 0; mi < NMI; ++mi) {
-          if (ni < 4)
-            part[ni & 1][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                af[mi], bfr[ni & 1], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-          if (ni > 0) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              acc[mi][ni - 1][v] =
-                  __builtin_fmaf(part[(ni - 1) & 1][mi][v], sc[mi][v], acc[mi][ni - 1][v]);
-          }
-        }
+      for (int ni = 0; ni < 4; ++ni) {
+        const i32x4 y0 = *reinterpret_cast<const i32x4*>(b_lo + ni * 16 * 128);
+        const i32x4 y1 = *reinterpret_cast<const i32x4*>(b_hi + ni * 16 * 128);
+        bfr[ni] = __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     };
-    issue(0, smem);
-    if (nkb > 1) issue(1, smem + kStage);
-    int kb = 0;
-    for (; kb + 2 < nkb; ++kb) kblock(kb, std::true_type{}, std::false_type{});
-    if (kb + 1 < nkb) kblock(kb++, std::false_type{}, std::false_type{});
-    kblock(kb, std::false_type{}, std::true_type{});
+    // row scale times block scale of every accumulator row of this lane
+    auto read_scales = [&](int kb) {
+      const uint8_t* st = smem + (kb % kStages) * kStage;
+      const float* sA = reinterpret_cast<const float*>(st + kABytes + kBBytes) + wm * 64 + 4 * lk;
+      const float sb = s_bd[wn >> 1][kb];
+#pragma unroll
+      for (int mi = 0; mi < NMI; ++mi) sc[mi] = *reinterpret_cast<const f32x4*>(sA + mi * 16) * sb;
+    };
+    auto mfma = [&]() {
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < NMI; ++mi)
+          part[ni][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af[mi], bfr[ni], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+    };
+    auto fma = [&]() {
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < NMI; ++mi)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            acc[mi][ni][v] = __builtin_fmaf(part[ni][mi][v], sc[mi][v], acc[mi][ni][v]);
+    };
+    // scale FMAs of (column subtile, row subtile) pairs q0 .. q1 - 1
+    auto fma_pairs = [&](int q0, int q1) {
+#pragma unroll
+      for (int q = 0; q < 4 * NMI; ++q) {
+        if (q < q0 || q >= q1) continue;
+        const int ni = q / NMI, mi = q - ni * NMI;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          acc[mi][ni][v] = __builtin_fmaf(part[ni][mi][v], sc[mi][v], acc[mi][ni][v]);
+      }
+    };
+    // The VALU / memory phase, in segments the compiler may not reorder: the
+    // fragment reads of K block kb_read first (their registers are free once
+    // the MFMAs are issued); then eight slices of the scale FMAs with one copy
+    // of a later stage before each of the first six, so the address unit
+    // drains while the FMAs run; last the scales of kb_read, whose registers
+    // the FMAs free.
+    auto xphase = [&](auto issue_c, auto fma_c, int kb_issue, uint8_t* slot, int kb_read) {
+      constexpr bool ISSUE = decltype(issue_c)::value, FMA = decltype(fma_c)::value;
+      if (ISSUE && wave < 2) issue_part(kb_issue, slot, 3);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (NMI > 0) read_frags(kb_read);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if constexpr (ISSUE) {
+          if (i < 6) issue_one(kb_issue, slot, i);
+        }
+        if constexpr (FMA && NMI > 0) fma_pairs(i * 4 * NMI / 8, (i + 1) * 4 * NMI / 8);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (NMI > 0) read_scales(kb_read);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // end of an E phase: this wave's copies of stage kb + 1 have landed
+    // (those of stage kb + 2 may be in flight) and its LDS reads are done.
+    // (After E_0 the copies still in flight are the A part of stage 2 only:
+    // the prologue requests the B parts of stages 0-2 first.)
+    auto end_e = [&](int kb) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (kb + 2 >= nkb) {
+        wait_and_barrier<0>();
+      } else if (kb == 0) {
+        if (n_w == 7) wait_and_barrier<3>(); else wait_and_barrier<2>();
+      } else {
+        if (n_w == 7) wait_and_barrier<7>(); else wait_and_barrier<6>();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto end_o = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // every wave requests stages 0-2 (the B parts first: they do not wait
+    // for the row map), then waits for stage 0
+    const int npro = min(nkb, kStages);
+    for (int st = 0; st < npro; ++st) {
+      issue_part(st, smem + st * kStage, 1);
+      issue_part(st, smem + st * kStage, 2);
+    }
+    for (int st = 0; st < npro; ++st) {
+      issue_part(st, smem + st * kStage, 0);
+      issue_part(st, smem + st * kStage, 3);
+    }
+    if (nkb > 2) {
+      if (n_w == 7) wait_and_barrier<6>(); else wait_and_barrier<4>();
+    } else if (nkb > 1) {
+      if (n_w == 7) wait_and_barrier<3>(); else wait_and_barrier<2>();
+    } else {
+      wait_and_barrier<0>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr std::true_type yes{};
+    constexpr std::false_type no{};
+    // (The loops are split where the copies stop, so no phase holds a branch;
+    // after the last K block, group 0 reads a stale stage it does not use.)
+    if (!g1) {
+      if constexpr (NMI > 0) {
+        read_frags(0);
+        read_scales(0);
+      }
+      int kb = 0;
+      for (; kb + 3 < nkb; ++kb) {
+        mfma();                                                         // E_kb
+        end_e(kb);
+        xphase(yes, yes, kb + 3, smem + (kb % kStages) * kStage, kb + 1);   // O_kb
+        end_o();
+      }
+      for (; kb < nkb; ++kb) {
+        mfma();
+        end_e(kb);
+        xphase(no, yes, 0, smem, min(kb + 1, nkb - 1));
+        end_o();
+      }
+    } else {
+      xphase(no, no, 0, smem, 0);                                       // E_0
+      end_e(0);
+      mfma();                                                           // O_0
+      end_o();
+      int kb = 1;
+      for (; kb + 2 < nkb; ++kb) {
+        xphase(yes, yes, kb + 2, smem + ((kb + 2) % kStages) * kStage, kb);   // E_kb
+        end_e(kb);
+        mfma();                                                         // O_kb
+        end_o();
+      }
+      for (; kb < nkb; ++kb) {
+        xphase(no, yes, 0, smem, kb);
+        end_e(kb);
+        mfma();
+        end_o();
+      }
+      fma();
+    }
   };
   const int nmi = wave_cols ? clampi((wave_rows + 15) >> 4, 0, 4) : 0;
   switch (__builtin_amdgcn_readfirstlane(nmi)) {
@@ -380,7 +498,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     uint8_t* otile = smem + 65536 + 2048;                          // [128][128] codes
     const bool gate_wave = wn < 2;
     const int partner = gate_wave ? wave + 4 : wave - 4;           // wn +- 2
-    const int give0 = gate_wave ? 2 : 0;                           // subtiles handed over
     const int keep0 = gate_wave ? 0 : 2;                           // subtiles kept
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
@@ -388,7 +505,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          ex[(wave * 32 + (mi * 2 + j) * 4 + v) * 64 + lane] = acc[mi][give0 + j][v];
+          ex[(wave * 32 + (mi * 2 + j) * 4 + v) * 64 + lane] =
+              gate_wave ? acc[mi][2 + j][v] : acc[mi][j][v];   // static indices: acc stays in registers
     __syncthreads();
     float h[4][2][4];
 #pragma unroll
@@ -399,7 +517,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
         float mx = 0.0f;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const float mine = acc[mi][keep0 + j][v];
+          const float mine = gate_wave ? acc[mi][j][v] : acc[mi][2 + j][v];
           const float other = ex[(partner * 32 + (mi * 2 + j) * 4 + v) * 64 + lane];
           const float gt = gate_wave ? mine : other;
           const float u = gate_wave ? other : mine;
@@ -407,25 +525,30 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
           h[mi][j][v] = gt * sg * u;
           mx = fmaxf(mx, fabsf(h[mi][j][v]));
         }
-        mx = group_max<16>(mx);
+        mx = row_max16(mx);
         if (lrow == 0) red[wn * 128 + row] = mx;
       }
     __syncthreads();
+    // one thread per row forms the tile's scale (two divisions) and stores d
     const int ld_d = p.n_out / BN;  // h scale row stride (h has n_out/2 columns)
+    float* s_m = reinterpret_cast<float*>(smem + 65536 + 2048 + 16384);   // [128] multipliers
+    if (tid < BM) {
+      float m, d;
+      tile_scale(fmaxf(fmaxf(red[tid], red[128 + tid]), fmaxf(red[256 + tid], red[384 + tid])), m, d);
+      s_m[tid] = m;
+      if (tid < rows_valid) p.out_d[(long long)(row0 + m0 + tid) * ld_d + n_tile] = d;
+    }
+    __syncthreads();
     const int hc = (wn & 1) * 64;   // this wave's 64-column half of the h tile
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = wm * 64 + mi * 16 + 4 * lk + v;
-        float m, d;
-        tile_scale(fmaxf(fmaxf(red[row], red[128 + row]), fmaxf(red[256 + row], red[384 + row])),
-                   m, d);
+        const float m = s_m[row];
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           otile[row * 128 + hc + (keep0 + j) * 16 + lrow] = (uint8_t)quant_code(h[mi][j][v], m);
-        if (wn == 0 && lrow == 0 && row < rows_valid)
-          p.out_d[(long long)(row0 + m0 + row) * ld_d + n_tile] = d;
       }
     __syncthreads();
     uint8_t* out = static_cast<uint8_t*>(p.out);
