@@ -18,8 +18,9 @@ a float32 rounding point).  It follows these pages, cited by title and section:
         selection equations, the bias thermostat and its flowchart) and
         section V (FP8 mixed precision, Figure 6 and details 1-4).
   [DF]  "DeepSeek-V3 Technical Report" (deepforge.srivtx.xyz) -- part 1
-        "Per-tile FP8 scaling" and "Balancing without a balance loss", and
-        part 4 "Build it yourself" (success criteria).
+        ("FP8 training, from first principles", "Per-tile FP8 scaling",
+        "Balancing without a balance loss") and part 4 "Build it yourself"
+        (success criteria).
 
 Modules:
   e4m3     OCP E4M3 codec, written twice (table search and arithmetic).
@@ -30,6 +31,7 @@ Modules:
   bias     sign-based bias update.
   balance  sequence-wise balance statistic (f_i P_i per sequence).
   layer    the whole layer chained from the pieces above.
+  backward FP8 input-gradient and weight-gradient GEMMs (token-tile quantiser).
 
 Parity status: every function above is pinned by ``tests/test_oracle_*.py``
 against closed forms, brute force, invariants or library special cases; none
