@@ -11,8 +11,9 @@ device, resident in HBM before the timed region.
 Prints ONE JSON line.  Default workload: the DeepSeek-V3-shaped layer at
 prefill size (T = 8192, H 7168, 256 routed experts top-8 + 1 shared, I 2048).
 Other workloads: decode (T = 512), skew (T = 32768, ten batches cycled, load
-max/mean reported), tiny, and routing (T = 16384: router, top-k, permutation
-and bias update only).  The timed region is K steps with an event pair around
+max/mean reported), tiny, routing (T = 16384: router, top-k, permutation and
+bias update only), and backward (the FP8 Dgrad and Wgrad GEMMs of both expert
+GEMMs at the prefill shape, on synthetic upstream gradients).  The timed region is K steps with an event pair around
 every launch on the launch stream; per-kernel times are the means of those.
 --router-fp8 swaps in the opt-in FP8 router (x quantised before routing); the
 routing workload also times the other router on the same batch and reports
@@ -77,7 +78,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill",
-                    choices=["prefill", "decode", "skew", "routing", "tiny"])
+                    choices=["prefill", "decode", "skew", "routing", "tiny", "backward"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--router-fp8", action="store_true",
                     help="the opt-in FP8 router (x quantised 1x128 first, Wr 128x128) in place "
@@ -280,6 +281,180 @@ def bench_routing(args, w, moe, torch, gen, wr, bias, st):
     print(json.dumps(res))
 
 
+def bench_backward(args, w, moe, torch, gen, lay, st):
+    """The FP8 backward GEMMs of the expert layer at the prefill shape.  A step:
+      Dgrad2  dH = dOut W2           (dOut quantised 1x128; W2 transposed once)
+      Wgrad2  dW2_g = dOut_g^T h_g   (128-token tiles of dOut and h)
+      Dgrad1  dU = dA W1             (dA: gradient at the GEMM1 output)
+      Wgrad1  dW1_g = dA_g^T x_g     (128-token tiles of dA and the gathered x)
+    with every quantisation in the step.  The upstream gradients dOut and dA
+    and the SwiGLU output h are seeded synthetic tensors; the expert groups are
+    those of the forward routing of the workload's batch.  Weight gradients are
+    float32, input gradients bf16."""
+    import synth
+    dev = lay.y.device
+    x = gen(w.x_spec())
+    lay.route(x)
+    lay.permute()
+    torch.cuda.synchronize()
+    T, H, I, G, R = w.T, w.H, w.I, w.G, lay.R
+    off = lay.offsets[:G + 1].contiguous()
+    x_rows = x.index_select(0, lay.token_of.long())                  # the gathered GEMM1 input
+    dout = gen(synth.Spec(synth.T_DOUT, (R, H), synth.NORMAL, 1e-3))
+    d_a = gen(synth.Spec(synth.T_DA, (R, 2 * I), synth.NORMAL, 1e-3))
+    h = gen(synth.Spec(synth.T_H, (R, I), synth.NORMAL, 1.0))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    w1t = moe.fp8_transpose_128x128(lay.w.w1q, lay.w.w1d)
+    w2t = moe.fp8_transpose_128x128(lay.w.w2q, lay.w.w2d)
+    e1.record(st)
+    torch.cuda.synchronize()
+    t_transpose = e0.elapsed_time(e1)
+    e = dict(device=dev)
+    ldt = moe.tokens_padded_width(R, G)
+    dq = (torch.empty(R, H, dtype=torch.uint8, **e), torch.empty(R, H // 128, dtype=torch.float32, **e))
+    aq = (torch.empty(R, 2 * I, dtype=torch.uint8, **e),
+          torch.empty(R, 2 * I // 128, dtype=torch.float32, **e))
+    d_h = torch.empty(R, I, dtype=torch.bfloat16, **e)
+    d_u = torch.empty(R, H, dtype=torch.bfloat16, **e)
+
+    def tok(C):
+        return (torch.empty(C, ldt, dtype=torch.uint8, **e),
+                torch.empty(C, ldt // 128, dtype=torch.float32, **e),
+                torch.empty(G + 1, dtype=torch.int32, **e))
+    t_dout, t_h, t_da, t_x = tok(H), tok(I), tok(2 * I), tok(H)
+    dw2 = torch.empty(G, H, I, dtype=torch.float32, **e)
+    dw1 = torch.empty(G, 2 * I, H, dtype=torch.float32, **e)
+    E_BF16 = moe.MOE_EPI_BF16
+
+    def tq(src, dst):
+        moe.fp8_quant_tokens_128(src, off, ldt=ldt, xt_q=dst[0], xt_d=dst[1], pad_offsets=dst[2])
+
+    names = ["quant_dout", "dgrad2", "tok_dout", "tok_h", "wgrad2",
+             "quant_da", "dgrad1", "tok_da", "tok_x", "wgrad1"]
+    fns = [lambda: moe.fp8_quant_1x128(dout, q=dq[0], d=dq[1]),
+           lambda: moe.moe_grouped_gemm_fp8(dq[0], dq[1], w2t[0], w2t[1], off, R, E_BF16, out=d_h),
+           lambda: tq(dout, t_dout), lambda: tq(h, t_h),
+           lambda: moe.moe_grouped_wgrad_fp8(t_dout[0], t_dout[1], t_h[0], t_h[1], t_dout[2], out=dw2),
+           lambda: moe.fp8_quant_1x128(d_a, q=aq[0], d=aq[1]),
+           lambda: moe.moe_grouped_gemm_fp8(aq[0], aq[1], w1t[0], w1t[1], off, R, E_BF16, out=d_u),
+           lambda: tq(d_a, t_da), lambda: tq(x_rows, t_x),
+           lambda: moe.moe_grouped_wgrad_fp8(t_da[0], t_da[1], t_x[0], t_x[1], t_da[2], out=dw1)]
+
+    def step(evs=None):
+        for i, f in enumerate(fns):
+            if evs is not None:
+                evs[i][0].record(st)
+            f()
+            if evs is not None:
+                evs[i][1].record(st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in names] for _ in range(args.steps)]
+    e0.record(st)
+    for i in range(args.steps):
+        step(evs[i])
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    kern = {n: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1])
+                              for i in range(args.steps)]))
+            for j, n in enumerate(names)}
+    rpad = int(t_dout[2][-1].item())
+    nb = rpad // 128
+    # algorithmic work of each GEMM: operands read once, output written once
+    work = {
+        "dgrad2": (2.0 * R * H * I,
+                   R * H + R * (H // 128) * 4 + G * H * I + G * (H // 128) * (I // 128) * 4 + R * I * 2),
+        "wgrad2": (2.0 * R * H * I, (H + I) * (rpad + nb * 4) + G * H * I * 4),
+        "dgrad1": (2.0 * R * 2 * I * H,
+                   R * 2 * I + R * (2 * I // 128) * 4 + G * 2 * I * H
+                   + G * (2 * I // 128) * (H // 128) * 4 + R * H * 2),
+        "wgrad1": (2.0 * R * 2 * I * H, (2 * I + H) * (rpad + nb * 4) + G * 2 * I * H * 4),
+    }
+    gemm_flops = sum(f for f, _ in work.values())
+    gemm_ms = sum(kern[n] for n in work)
+    dom = max(work, key=lambda n: kern[n])
+    fl, by = work[dom]
+    t_dom = kern[dom] * 1e-3
+    if by / (HBM_PEAK_GBS * 1e9) >= fl / (FP8_PEAK_TFLOPS * 1e12):
+        roof = {"bound": "hbm", "achieved": round(by / t_dom / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(by / t_dom / 1e9 / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(fl / t_dom / 1e12, 2), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(fl / t_dom / 1e12 / FP8_PEAK_TFLOPS, 4)}
+    kname = {"wgrad1": "wgrad_kernel (dW1)", "wgrad2": "wgrad_kernel (dW2)",
+             "dgrad1": "grouped_gemm_kernel<0> (dX, Dgrad of W1)",
+             "dgrad2": "grouped_gemm_kernel<0> (dH, Dgrad of W2)"}[dom]
+    roof.update({"traffic": None, "kernel": kname, "kernel_avg_ms": round(kern[dom], 4),
+                 "algorithmic_bytes_per_launch": by, "algorithmic_flops_per_launch": fl,
+                 "mfma_tflops": round(fl / t_dom / 1e12, 2),
+                 "hbm_gbs": round(by / t_dom / 1e9, 1)})
+    res = {
+        "metric": "MoE layer FP8 backward GEMMs tokens/s (Dgrad + Wgrad of both expert GEMMs) "
+                  "at V3 shape, 1 GPU",
+        "value": round(T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded upstream gradients and h generated on the device; expert "
+                "groups from the forward routing of the prefill batch)",
+        "config": {"workload": f"backward of the prefill layer's expert GEMMs: T={T} tokens, "
+                               f"{R} expert rows, hidden {H}, {w.N} routed experts top-{w.k} + 1 "
+                               f"shared, SwiGLU intermediate {I}",
+                   "T": T, "R": R, "H": H, "I": I, "G": G, "padded_token_columns": rpad},
+        "roofline": roof,
+        "gemm_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2),
+        "gemm_frac_fp8_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+        "kernel_ms": {n: round(v, 4) for n, v in kern.items()},
+        "per_gemm": {n: {"ms": round(kern[n], 4),
+                         "TFLOPs": round(f / (kern[n] * 1e-3) / 1e12, 2),
+                         "GBps": round(b / (kern[n] * 1e-3) / 1e9, 1)} for n, (f, b) in work.items()},
+        "weight_transpose_ms": round(t_transpose, 3),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_backward(w, R)
+    print(json.dumps(res))
+
+
+def cpu_baseline_backward(w, R):
+    """The oracle's four backward GEMMs with their quantisation on a sample of
+    512 expert rows in two groups of 256 (the mean routed-expert load), timed
+    on the host and scaled per row to the step's R rows."""
+    import synth
+    from oracle import backward, quant
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    H, I, S = w.H, w.I, 512
+    off = np.array([0, 256, 512])
+    rows = np.arange(S)
+    f64 = synth.as_f64
+    dout = f64(synth.generate(synth.Spec(synth.T_DOUT, (R, H), synth.NORMAL, 1e-3), w.seed, rows=rows))
+    d_a = f64(synth.generate(synth.Spec(synth.T_DA, (R, 2 * I), synth.NORMAL, 1e-3), w.seed, rows=rows))
+    h = f64(synth.generate(synth.Spec(synth.T_H, (R, I), synth.NORMAL, 1.0), w.seed, rows=rows))
+    x = f64(synth.generate(w.x_spec(), w.seed, rows=rows))
+    w1q, w1d = quant.quant_128x128(f64(synth.generate(w.w1_spec(), w.seed, rows=np.arange(2 * I))))
+    w2q, w2d = quant.quant_128x128(f64(synth.generate(w.w2_spec(), w.seed, rows=np.arange(H))))
+    t0 = time.perf_counter()
+    for g in range(2):
+        sl = slice(off[g], off[g + 1])
+        backward.dgrad(dout[sl], w2q, w2d)
+        backward.dgrad(d_a[sl], w1q, w1d)
+    backward.wgrad(dout, h, off)
+    backward.wgrad(d_a, x, off)
+    dt = time.perf_counter() - t0
+    return {"value": w.T / (dt / S * R), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{S} expert rows in two groups of 256: Dgrad and Wgrad of both expert "
+                      f"GEMMs with their quantisers, scaled per row to {R} rows",
+            "measured_s": round(dt, 3)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -292,7 +467,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    w = synth.WORKLOADS[args.workload]
+    # the backward workload runs the prefill layer's expert GEMMs backwards
+    w = synth.WORKLOADS["prefill" if args.workload == "backward" else args.workload]
     dev = torch.device("cuda:0")
 
     def gen(spec, seed=w.seed):
@@ -325,6 +501,9 @@ def main():
     weights = moe.MoEWeights(wr, bias, w1q=w1q, w1d=w1d, w2q=w2q, w2d=w2d,
                              router_fp8=args.router_fp8)
     lay = moe.MoELayer(weights, w.T, w.k, w.gamma, device=dev, router_fp8=args.router_fp8)
+    if args.workload == "backward":
+        bench_backward(args, w, moe, torch, gen, lay, st)
+        return
     # the batches of the workload (one for most; the skewed-load workload has
     # ten, batch b drawn with seed offset b); step i runs batch i % batches
     xs = [gen(w.x_spec(b)) for b in range(w.batches)]

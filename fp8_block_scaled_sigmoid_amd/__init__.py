@@ -45,6 +45,7 @@ class GemmArgs(ctypes.Structure):
 _lib = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int
+_LL = ctypes.c_longlong
 
 
 def lib():
@@ -66,6 +67,9 @@ def lib():
             "moe_combine": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P],
             "moe_bias_update": [_P, _P, _I, _I, _I, ctypes.c_float, _P],
             "moe_seq_balance_loss": [_P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P],
+            "fp8_transpose_128x128": [_P, _P, _I, _I, _I, _P, _P, _P],
+            "fp8_quant_tokens_128": [_P, _I, _I, _I, _LL, _P, _I, _P, _P, _LL, _P, _P],
+            "moe_grouped_wgrad_fp8": [_P, _P, _LL, _I, _P, _P, _LL, _I, _P, _I, _P, _P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -255,6 +259,81 @@ def moe_grouped_gemm_fp8(a_q, a_d, b_q, b_d, group_offsets, total_rows, epilogue
                     row_scale.data_ptr() if row_scale is not None else None)
     _check("moe_grouped_gemm_fp8", lib().moe_grouped_gemm_fp8(ctypes.byref(args), _stream(stream)))
     return out, out_d
+
+
+def fp8_transpose_128x128(w_q, w_d, wt_q=None, wt_d=None, stream=None):
+    """Exact transpose of 128x128 block-quantised weights: w_q uint8
+    [B, rows, cols], w_d float32 [B, rows/128, cols/128] -> (wt_q [B, cols,
+    rows], wt_d [B, cols/128, rows/128]).  The B operand of Dgrad."""
+    if w_q.dim() == 2:
+        w_q, w_d = w_q.unsqueeze(0), w_d.unsqueeze(0)
+    B, rows, cols = w_q.shape
+    _dev(w_q, torch.uint8, "w_q"), _dev(w_d, torch.float32, "w_d")
+    dev = w_q.device
+    wt_q = torch.empty(B, cols, rows, dtype=torch.uint8, device=dev) if wt_q is None else wt_q
+    wt_d = torch.empty(B, cols // 128, rows // 128, dtype=torch.float32, device=dev) \
+        if wt_d is None else wt_d
+    _check("fp8_transpose_128x128", lib().fp8_transpose_128x128(
+        _ptr(w_q), _ptr(w_d), B, rows, cols, _ptr(wt_q), _ptr(wt_d), _stream(stream)))
+    return wt_q, wt_d
+
+
+def tokens_padded_width(rows, num_groups):
+    """Row stride (bytes) that holds any token-tile layout of `rows` tokens in
+    `num_groups` groups: a multiple of 128, at least rows + 127 * num_groups."""
+    return (rows + 127 * num_groups + 127) // 128 * 128
+
+
+def fp8_quant_tokens_128(x, group_offsets, ldt=None, xt_q=None, xt_d=None, pad_offsets=None,
+                         stream=None):
+    """Token-tile quantiser (Wgrad operands).  x [rows, cols] bf16 or float32
+    in expert-grouped row order, group_offsets int32 [G+1] -> (xt_q uint8
+    [cols, ldt], xt_d float32 [cols, ldt/128], pad_offsets int32 [G+1])."""
+    rows, cols = x.shape
+    G = group_offsets.numel() - 1
+    dt = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}[x.dtype]
+    if x.stride(1) != 1:
+        raise ValueError("x: rows must be contiguous")
+    _dev(group_offsets, torch.int32, "group_offsets")
+    ldt = tokens_padded_width(rows, G) if ldt is None else ldt
+    dev = x.device
+    xt_q = torch.empty(cols, ldt, dtype=torch.uint8, device=dev) if xt_q is None else xt_q
+    xt_d = torch.empty(cols, ldt // 128, dtype=torch.float32, device=dev) if xt_d is None else xt_d
+    pad_offsets = torch.empty(G + 1, dtype=torch.int32, device=dev) if pad_offsets is None \
+        else pad_offsets
+    _check("fp8_quant_tokens_128", lib().fp8_quant_tokens_128(
+        _ptr(x), dt, rows, cols, x.stride(0), _ptr(group_offsets), G, _ptr(xt_q), _ptr(xt_d),
+        ldt, _ptr(pad_offsets), _stream(stream)))
+    return xt_q, xt_d, pad_offsets
+
+
+def moe_grouped_wgrad_fp8(a_q, a_d, b_q, b_d, pad_offsets, out=None, stream=None):
+    """Wgrad grouped GEMM: out[g] = dY_g^T X_g (float32 [G, N, K]) from the
+    token-tile operands a (dY^T, [N, lda]) and b (X^T, [K, ldb])."""
+    N, lda = a_q.shape
+    K, ldb = b_q.shape
+    G = pad_offsets.numel() - 1
+    for t, dt, n in ((a_q, torch.uint8, "a_q"), (a_d, torch.float32, "a_d"),
+                     (b_q, torch.uint8, "b_q"), (b_d, torch.float32, "b_d"),
+                     (pad_offsets, torch.int32, "pad_offsets")):
+        _dev(t, dt, n)
+    out = torch.empty(G, N, K, dtype=torch.float32, device=a_q.device) if out is None else out
+    _check("moe_grouped_wgrad_fp8", lib().moe_grouped_wgrad_fp8(
+        _ptr(a_q), _ptr(a_d), lda, N, _ptr(b_q), _ptr(b_d), ldb, K, _ptr(pad_offsets), G,
+        _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_grouped_dgrad_fp8(dy, wt_q, wt_d, group_offsets, epilogue=MOE_EPI_BF16, dy_q=None,
+                          dy_d=None, out=None, stream=None):
+    """Dgrad: dX = dY W per group.  dy [R, N] bf16 or float32 (grouped rows),
+    wt_q/wt_d the transposed weights from fp8_transpose_128x128 ([G, K, N]).
+    dY is quantised 1x128 (fp8_quant_1x128), then the grouped FP8 GEMM runs
+    with the bf16 or float32 epilogue.  Returns dX [R, K]."""
+    dy_q, dy_d = fp8_quant_1x128(dy, q=dy_q, d=dy_d, stream=stream)
+    out, _ = moe_grouped_gemm_fp8(dy_q, dy_d, wt_q, wt_d, group_offsets, dy.shape[0], epilogue,
+                                  out=out, stream=stream)
+    return out
 
 
 def moe_combine(out_rows, gate, row_of, shared_row0, residual=None, y=None, stream=None):

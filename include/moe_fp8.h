@@ -240,7 +240,6 @@ moe_status_t moe_combine(const void* out_rows_bf16, const float* gate, const int
 moe_status_t moe_bias_update(float* bias, const int32_t* counts, int N, int T, int k, float gamma,
                              hipStream_t stream);
 
-/* Human-readable name of a status code (static string). */
 /*
  * Sequence-wise balance statistic ([TP] section III, "The one small loss that
  * remains"; [VE] recipe step 4): for each sequence s (tokens seq_offsets[s] ..
@@ -257,6 +256,69 @@ moe_status_t moe_seq_balance_loss(const int32_t* topk_idx, const float* topk_gat
                                   const int32_t* seq_offsets, int n_seq, int T, int N, int k,
                                   float alpha, float* loss, hipStream_t stream);
 
+/*
+ * FP8 backward GEMMs of a linear layer Y = X W^T ([TP] section V, Figure 6:
+ * the input-gradient and weight-gradient GEMMs also take FP8 inputs and
+ * accumulate in FP32; detail 3: E4M3 on every tensor; detail 4 and [DF] part 1
+ * "FP8 training, from first principles": gradients kept in higher precision).
+ *
+ * Dgrad, dX = dY W, is moe_grouped_gemm_fp8 with a_q/a_d = fp8_quant_1x128 of
+ * dY (tokens x output channels, grouped like the forward rows) and b_q/b_d =
+ * the transposed weight codes and scales written by fp8_transpose_128x128.
+ *
+ * fp8_transpose_128x128: exact transpose of 128x128 block-quantised weights,
+ * w_q E4M3 [batch, rows, cols] with w_d float [batch, rows/128, cols/128] ->
+ * wt_q [batch, cols, rows], wt_d [batch, cols/128, rows/128] (a block's codes
+ * transposed, its scale unchanged).  Requires rows % 128 == 0,
+ * cols % 128 == 0; code pointers 16-byte aligned.
+ */
+moe_status_t fp8_transpose_128x128(const uint8_t* w_q, const float* w_d, int batch, int rows,
+                                   int cols, uint8_t* wt_q, float* wt_d, hipStream_t stream);
+
+/*
+ * Token-tile quantiser for Wgrad (the contraction runs over tokens, so each
+ * operand gets one scale per 128 consecutive tokens of one channel; a tile
+ * never spans two experts).  x [rows, cols] (bf16 or float, row stride ldx
+ * elements) in expert-grouped row order, group g = rows group_offsets[g] ..
+ * group_offsets[g+1]-1 (device int32 [num_groups + 1], clamped into
+ * [0, rows]).  Writes pad_offsets int32 [num_groups + 1] (group g's first
+ * padded token column, P_g = sum over earlier groups of 128 * ceil(rows_g /
+ * 128); pad_offsets[G] = the padded length) and, transposed, xt_q E4M3
+ * [cols, ldt] (column P_g + j of channel c = token group_offsets[g] + j) and
+ * xt_d float [cols, ldt/128].  A group's last tile covers its remaining
+ * tokens only: its amax is over them and the other positions are code 0.
+ * Per tile: m = fl32(448/amax), d = fl32(amax/448), code = E4M3(x*m) (zero
+ * tile: codes 0, d = 1).  Columns past pad_offsets[G] are not written.
+ * Requires cols % 64 == 0, ldt % 128 == 0, ldt >= rows + 127 * num_groups,
+ * 1 <= num_groups <= 1025, ceil(rows/128) + num_groups <= 65535
+ * (MOE_ERR_UNSUPPORTED otherwise); x and xt_q 16-byte aligned.
+ */
+moe_status_t fp8_quant_tokens_128(const void* x, moe_dtype_t dtype, int rows, int cols,
+                                  long long ldx, const int32_t* group_offsets, int num_groups,
+                                  uint8_t* xt_q, float* xt_d, long long ldt, int32_t* pad_offsets,
+                                  hipStream_t stream);
+
+/*
+ * Wgrad grouped GEMM: for every expert g,
+ *   out[g][n][k] = sum over the 128-token tiles c of group g of
+ *                  d_A[n, c] d_B[k, c] sum_{j in c} q_A[n, j] q_B[k, j]
+ * i.e. dW_g = dY_g^T X_g from the token-tile operands of
+ * fp8_quant_tokens_128: a_q [n_rows, lda] / a_d [n_rows, lda/128] (dY^T),
+ * b_q [k_rows, ldb] / b_d [k_rows, ldb/128] (X^T), pad_offsets int32
+ * [num_groups + 1] (device, multiples of 128, clamped to the operands'
+ * width).  out float [num_groups, n_rows, k_rows]; an empty expert gets zeros.
+ * Each tile product comes from the FP8 MFMA in float and is scaled and added
+ * with float multiplies and fused multiply-adds, tiles in token order.
+ * Requires n_rows % 128 == 0, k_rows % 128 == 0, lda and ldb multiples of 128,
+ * n_rows * lda < 2^31 and k_rows * ldb < 2^31 (MOE_ERR_UNSUPPORTED); code
+ * pointers and out 16-byte aligned.
+ */
+moe_status_t moe_grouped_wgrad_fp8(const uint8_t* a_q, const float* a_d, long long lda,
+                                   int n_rows, const uint8_t* b_q, const float* b_d,
+                                   long long ldb, int k_rows, const int32_t* pad_offsets,
+                                   int num_groups, float* out, hipStream_t stream);
+
+/* Human-readable name of a status code (static string). */
 const char* moe_status_str(moe_status_t status);
 /* hipError_t of the most recent MOE_ERR_HIP on this thread (0 if none). */
 int moe_last_hip_error(void);

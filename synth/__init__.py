@@ -43,6 +43,9 @@ UNIFORM = 1
 
 # tensor ids
 T_X, T_WR, T_BIAS, T_W1, T_W2, T_PERM, T_OUTLIER, T_SCORES, T_ROWS, T_GATES = range(1, 11)
+# upstream gradients of the backward workload: d(layer output rows), d(GEMM1
+# output), and the SwiGLU output h
+T_DOUT, T_DA, T_H = range(11, 14)
 
 
 def mix64_int(z):

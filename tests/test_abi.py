@@ -33,7 +33,8 @@ def test_header_declares_the_layer_calls():
               "moe_topk_from_scores", "moe_permute",
               "moe_permute_workspace_bytes", "fp8_quant_1x128", "fp8_quant_128x128",
               "moe_grouped_gemm_fp8", "moe_combine", "moe_bias_update", "moe_status_str",
-              "moe_last_hip_error"]:
+              "moe_last_hip_error", "fp8_transpose_128x128", "fp8_quant_tokens_128",
+              "moe_grouped_wgrad_fp8"]:
         assert n in names, n
 
 
@@ -108,6 +109,22 @@ def test_validation_before_any_launch(lib):
     assert lib.moe_seq_balance_loss(None, None, None, 2, 8, 2000, 2, 1e-4, None, None) == 2
     assert lib.moe_seq_balance_loss(None, None, None, 0, 8, 16, 2, 1e-4, None, None) == 0
     assert lib.moe_seq_balance_loss(None, None, dummy, 2, 8, 16, 2, 1e-4, dummy, None) == 1
+    LL = ctypes.c_longlong
+    lib.fp8_transpose_128x128.argtypes = [P, P, I, I, I, P, P, P]
+    assert lib.fp8_transpose_128x128(None, None, 1, 100, 128, None, None, None) == 2
+    assert lib.fp8_transpose_128x128(None, None, 0, 128, 128, None, None, None) == 0
+    assert lib.fp8_transpose_128x128(None, None, 1, 128, 128, None, None, None) == 1
+    assert lib.fp8_transpose_128x128(ctypes.c_void_p(8), dummy, 1, 128, 128, dummy, dummy, None) == 3
+    lib.fp8_quant_tokens_128.argtypes = [P, I, I, I, LL, P, I, P, P, LL, P, P]
+    assert lib.fp8_quant_tokens_128(None, 0, 300, 100, 100, None, 2, None, None, 640, None, None) == 2  # cols % 64
+    assert lib.fp8_quant_tokens_128(None, 0, 300, 64, 64, None, 2, None, None, 512, None, None) == 2   # ldt too small
+    assert lib.fp8_quant_tokens_128(None, 0, 300, 64, 64, None, 2, None, None, 640, None, None) == 1   # NULL offsets
+    assert lib.fp8_quant_tokens_128(None, 2, 300, 64, 64, dummy, 2, None, None, 640, dummy, None) == 6  # dtype
+    lib.moe_grouped_wgrad_fp8.argtypes = [P, P, LL, I, P, P, LL, I, P, I, P, P]
+    assert lib.moe_grouped_wgrad_fp8(None, None, 256, 100, None, None, 256, 128, None, 2, None, None) == 2
+    assert lib.moe_grouped_wgrad_fp8(None, None, 200, 128, None, None, 256, 128, None, 2, None, None) == 2
+    assert lib.moe_grouped_wgrad_fp8(None, None, 256, 128, None, None, 256, 128, None, 2, None, None) == 1
+    assert lib.moe_grouped_wgrad_fp8(None, None, 256, 0, None, None, 256, 128, None, 2, None, None) == 0
     lib.moe_permute_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_permute_workspace_bytes.argtypes = [I, I, I]
     assert lib.moe_permute_workspace_bytes(513, 256, 8) == 3 * 256 * 4
