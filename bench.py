@@ -422,7 +422,7 @@ def bench_backward(args, w, moe, torch, gen, lay, st):
 
 def cpu_baseline_backward(w, R):
     """The oracle's four backward GEMMs with their quantisation on a sample of
-    512 expert rows in two groups of 256 (the mean routed-expert load), timed
+    4096 expert rows in 16 groups of 256 (the mean routed-expert load), timed
     on the host and scaled per row to the step's R rows."""
     import synth
     from oracle import backward, quant
@@ -431,8 +431,8 @@ def cpu_baseline_backward(w, R):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
-    H, I, S = w.H, w.I, 512
-    off = np.array([0, 256, 512])
+    H, I, S = w.H, w.I, 4096
+    off = np.arange(0, S + 1, 256)
     rows = np.arange(S)
     f64 = synth.as_f64
     dout = f64(synth.generate(synth.Spec(synth.T_DOUT, (R, H), synth.NORMAL, 1e-3), w.seed, rows=rows))
@@ -442,7 +442,7 @@ def cpu_baseline_backward(w, R):
     w1q, w1d = quant.quant_128x128(f64(synth.generate(w.w1_spec(), w.seed, rows=np.arange(2 * I))))
     w2q, w2d = quant.quant_128x128(f64(synth.generate(w.w2_spec(), w.seed, rows=np.arange(H))))
     t0 = time.perf_counter()
-    for g in range(2):
+    for g in range(off.size - 1):
         sl = slice(off[g], off[g + 1])
         backward.dgrad(dout[sl], w2q, w2d)
         backward.dgrad(d_a[sl], w1q, w1d)
@@ -450,7 +450,7 @@ def cpu_baseline_backward(w, R):
     backward.wgrad(d_a, x, off)
     dt = time.perf_counter() - t0
     return {"value": w.T / (dt / S * R), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{S} expert rows in two groups of 256: Dgrad and Wgrad of both expert "
+            "sample": f"{S} expert rows in 16 groups of 256: Dgrad and Wgrad of both expert "
                       f"GEMMs with their quantisers, scaled per row to {R} rows",
             "measured_s": round(dt, 3)}
 

@@ -190,12 +190,13 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(
 // ---------------------------------------------------------------------------
 // Wgrad grouped GEMM
 
-constexpr int kWM = 128, kWN = 256;                        // output tile: N rows x K columns
-constexpr int kWThreads = 512;
+constexpr int kWM = 128, kWN = 128;                        // output tile: N rows x K columns
+constexpr int kWThreads = 256;                             // 4 waves, 2 x 2 of 64 x 64
 constexpr int kWStage = kWM * 128 + kWN * 128 + (kWM + kWN) * 4;   // codes, then A and B scales
-constexpr int kWStages = 3;
-constexpr int kWLds = kWStages * kWStage;                  // 148.5 KiB
+constexpr int kWStages = 2;
 constexpr int kWOutStride = kWN + 4;                       // float stride of the output staging
+constexpr int kWLds = kWStages * kWStage > kWM * kWOutStride * 4 ? kWStages * kWStage
+                                                                  : kWM * kWOutStride * 4;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_bw(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
@@ -219,13 +220,18 @@ struct WgradParams {
 
 // Tile (g, n-tile, k-tile) of the list, XCD-aware like the forward GEMM: each
 // XCD takes a contiguous run, so one XCD works through one expert's operands.
-// 8 waves: wave (wm, wn) owns 64 x 64 outputs; per 128-token block, 16 FP8
-// MFMAs into zero accumulators, then acc += part * (d_A[row] * d_B[col]).
-__global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(WgradParams p) {
+// An expert's contraction is short (its tokens), so the float output write
+// dominates: the tile is 128 x 128 with 4 waves and two stages (67.6 KiB of
+// LDS), which lets two workgroups share a compute unit and overlap one's
+// loads with the other's write; the output is written with streaming
+// (non-temporal) stores.  Wave (wm, wn) owns 64 x 64 outputs; per 128-token
+// block, 16 FP8 MFMAs into zero accumulators, then acc += part * (d_A[row] *
+// d_B[col]).
+__global__ __launch_bounds__(kWThreads, 2) void wgrad_kernel(WgradParams p) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tn = p.N / kWM, tk = (p.K + kWN - 1) / kWN;
+  const int tn = p.N / kWM, tk = p.K / kWN;
   const int per_g = tn * tk;
   const long long total = (long long)p.G * per_g;
   const long long per_xcd = (total + 7) / 8;
@@ -235,12 +241,11 @@ __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(WgradParams p) {
   const int g = (int)(L / per_g);
   const int rem = (int)(L - (long long)g * per_g);
   const int n0 = (rem / tk) * kWM, k0 = (rem % tk) * kWN;
-  const bool half = p.K - k0 < kWN;
   const int lim = (int)min(p.lda, p.ldb) / 128 * 128;
   const int p0 = clampi_bw(p.pad[g], 0, lim), p1 = clampi_bw(p.pad[g + 1], p0, lim);
   const int nkb = (p1 - p0) / 128;
 
-  // copies: load j of wave w fills 1 KiB block 8 j + w (rows 8 (8 j + w) ..);
+  // copies: load j of wave w fills 1 KiB block 4 j + w (rows 8 (4 j + w) ..);
   // lane l: row + (l >> 3), swizzled chunk (l & 7) ^ ((row >> 1) & 7)
   const int chunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
   const int lrow8 = 8 * wave + (lane >> 3);
@@ -249,33 +254,29 @@ __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(WgradParams p) {
   const __amdgpu_buffer_rsrc_t rs_b = make_rsrc_bw(p.b_q, (int)(p.K * p.ldb));
   const __amdgpu_buffer_rsrc_t rs_sa = make_rsrc_bw(p.a_d, p.N * sa_stride * 4);
   const __amdgpu_buffer_rsrc_t rs_sb = make_rsrc_bw(p.b_d, p.K * sb_stride * 4);
-  int a_off[2], b_off[4];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) a_off[j] = (n0 + 64 * j + lrow8) * (int)p.lda + p0 + chunk * 16;
+  int a_off[4], b_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int jj = half ? (j & 1) : j;   // past K: repeat valid rows
-    b_off[j] = (k0 + 64 * jj + lrow8) * (int)p.ldb + p0 + chunk * 16;
+    a_off[j] = (n0 + 32 * j + lrow8) * (int)p.lda + p0 + chunk * 16;
+    b_off[j] = (k0 + 32 * j + lrow8) * (int)p.ldb + p0 + chunk * 16;
   }
-  // scales: waves 0-1 copy the 128 A-row scales, waves 2-5 the 256 B-row scales
-  int s_off = 0;
-  if (wave < 2) s_off = ((n0 + 64 * wave + lane) * sa_stride + p0 / 128) * 4;
-  else if (wave < 6) s_off = (min(k0 + 64 * (wave - 2) + lane, p.K - 1) * sb_stride + p0 / 128) * 4;
-  const int n_w = wave < 6 ? 7 : 6;
+  // scales: waves 0-1 copy the 128 A-row scales, waves 2-3 the 128 B-row scales
+  const int s_off = wave < 2 ? ((n0 + 64 * wave + lane) * sa_stride + p0 / 128) * 4
+                             : ((k0 + 64 * (wave - 2) + lane) * sb_stride + p0 / 128) * 4;
   auto issue = [&](int kb, uint8_t* st) {
     const int ko = kb * 128;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_ptr_t)(st + (8 * j + wave) * 1024), 16,
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_ptr_t)(st + (4 * j + wave) * 1024), 16,
                                                a_off[j], ko, 0, 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs_b, (lds_ptr_t)(st + kWM * 128 + (8 * j + wave) * 1024), 16, b_off[j], ko, 0, 0);
+          rs_b, (lds_ptr_t)(st + kWM * 128 + (4 * j + wave) * 1024), 16, b_off[j], ko, 0, 0);
     if (wave < 2)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs_sa, (lds_ptr_t)(st + (kWM + kWN) * 128 + wave * 256), 4, s_off, kb * 4, 0, 0);
-    else if (wave < 6)
+    else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs_sb, (lds_ptr_t)(st + (kWM + kWN) * 128 + kWM * 4 + (wave - 2) * 256), 4, s_off,
           kb * 4, 0, 0);
@@ -286,23 +287,17 @@ __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(WgradParams p) {
   const int sw = (lrow >> 1) & 7;
   const int frag_lo = lrow * 128 + ((lk ^ sw) << 4);
   const int frag_hi = lrow * 128 + (((lk + 4) ^ sw) << 4);
-  const bool live = !(half && wn >= 2);
   f32x4 acc[4][4];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // two stages: stage kb + 2 reuses kb's slot once every wave is done with it
   if (nkb > 0) issue(0, smem);
   if (nkb > 1) issue(1, smem + kWStage);
   for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + 1 < nkb) {
-      if (n_w == 7) wait_barrier_bw<7>(); else wait_barrier_bw<6>();
-    } else {
-      wait_barrier_bw<0>();
-    }
-    if (kb + 2 < nkb) issue(kb + 2, smem + ((kb + 2) % kWStages) * kWStage);
-    if (!live) continue;
+    if (kb + 1 < nkb) wait_barrier_bw<9>(); else wait_barrier_bw<0>();
     const uint8_t* st = smem + (kb % kWStages) * kWStage;
     const float* sA = reinterpret_cast<const float*>(st + (kWM + kWN) * 128) + wm * 64 + 4 * lk;
     const float* sB = reinterpret_cast<const float*>(st + (kWM + kWN) * 128 + kWM * 4) + wn * 64 + lrow;
@@ -325,6 +320,11 @@ __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(WgradParams p) {
       bfr[ni] = __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
       sbc[ni] = sB[ni * 16];
     }
+    if (kb + 2 < nkb) {
+      // every wave's fragment reads of this slot are done before it is refilled
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      issue(kb + 2, smem + (kb % kWStages) * kWStage);
+    }
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
@@ -337,8 +337,8 @@ __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(WgradParams p) {
       }
   }
   __syncthreads();
-  // stage the float tile in LDS (row stride 260 floats keeps the writes of a
-  // wave on distinct banks), then write whole 1 KiB output rows
+  // stage the float tile in LDS (row stride 132 floats keeps the writes of a
+  // wave on distinct banks), then stream whole 512-byte output rows
   float* o = reinterpret_cast<float*>(smem);
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
@@ -349,12 +349,11 @@ __global__ __launch_bounds__(kWThreads, 1) void wgrad_kernel(WgradParams p) {
         o[(wm * 64 + mi * 16 + 4 * lk + v) * kWOutStride + wn * 64 + ni * 16 + lrow] = acc[mi][ni][v];
   __syncthreads();
   float* out = p.out + ((long long)g * p.N + n0) * p.K + k0;
-  const int cols = half ? 128 : kWN;
+#pragma unroll 4
   for (int q = tid; q < kWM * (kWN / 4); q += kWThreads) {
     const int r = q / (kWN / 4), c4 = (q % (kWN / 4)) * 4;
-    if (c4 < cols)
-      *reinterpret_cast<float4*>(out + (long long)r * p.K + c4) =
-          *reinterpret_cast<const float4*>(o + r * kWOutStride + c4);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(o + r * kWOutStride + c4);
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out + (long long)r * p.K + c4));
   }
 }
 
@@ -437,7 +436,7 @@ extern "C" moe_status_t moe_grouped_wgrad_fp8(const uint8_t* a_q, const float* a
   WgradParams p;
   p.a_q = a_q; p.a_d = a_d; p.lda = lda; p.b_q = b_q; p.b_d = b_d; p.ldb = ldb;
   p.pad = pad_offsets; p.G = num_groups; p.N = n_rows; p.K = k_rows; p.out = out;
-  const long long tiles = (long long)num_groups * (n_rows / kWM) * ((k_rows + kWN - 1) / kWN);
+  const long long tiles = (long long)num_groups * (n_rows / kWM) * (k_rows / kWN);
   const long long grid = (tiles + 7) / 8 * 8;
   if (grid > 0x7FFFFFFFLL) return MOE_ERR_SHAPE;
   hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)grid), dim3(kWThreads), kWLds, stream, p);
