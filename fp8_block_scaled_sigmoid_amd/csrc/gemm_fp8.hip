@@ -308,6 +308,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     const int n_w = wave < 2 ? 7 : 6;          // copies per stage of this wave
     i32x8 af[4], bfr[4];
     f32x4 part[4][4], sc[4];
+    float sbv = 0.0f;
     // MFMA lane group lk takes the 16-byte K chunks lk and lk + 4 of its row,
     // for A and B alike (a fixed permutation of K inside the block, so the
     // dot product is unchanged); this keeps each ds_read_b128 free of LDS bank
@@ -333,13 +334,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
         bfr[ni] = __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     };
-    // row scale times block scale of every accumulator row of this lane
+    // the row scales of every accumulator row of this lane, and the block
+    // scale; they are multiplied in the next MFMA phase (scale_rows), so no
+    // phase waits for these reads
     auto read_scales = [&](int kb) {
       const uint8_t* st = smem + (kb % kStages) * kStage;
       const float* sA = reinterpret_cast<const float*>(st + kABytes + kBBytes) + wm * 64 + 4 * lk;
-      const float sb = s_bd[wn >> 1][kb];
+      sbv = s_bd[wn >> 1][kb];
 #pragma unroll
-      for (int mi = 0; mi < NMI; ++mi) sc[mi] = *reinterpret_cast<const f32x4*>(sA + mi * 16) * sb;
+      for (int mi = 0; mi < NMI; ++mi) sc[mi] = *reinterpret_cast<const f32x4*>(sA + mi * 16);
+    };
+    auto scale_rows = [&]() {
+#pragma unroll
+      for (int mi = 0; mi < NMI; ++mi) sc[mi] = sc[mi] * sbv;
     };
     auto mfma = [&]() {
 #pragma unroll
@@ -373,8 +380,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     // fragment reads of K block kb_read first (their registers are free once
     // the MFMAs are issued); then eight slices of the scale FMAs with one copy
     // of a later stage before each of the first six, so the address unit
-    // drains while the FMAs run; last the scales of kb_read, whose registers
-    // the FMAs free.
+    // drains while the FMAs run; last the row scales of kb_read, into the
+    // registers the FMAs free (nothing in this phase waits for them).
     auto xphase = [&](auto issue_c, auto fma_c, int kb_issue, uint8_t* slot, int kb_read) {
       constexpr bool ISSUE = decltype(issue_c)::value, FMA = decltype(fma_c)::value;
       if (ISSUE && wave < 2) issue_part(kb_issue, slot, 3);
@@ -443,12 +450,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
       int kb = 0;
       for (; kb + 3 < nkb; ++kb) {
         mfma();                                                         // E_kb
+        scale_rows();
         end_e(kb);
         xphase(yes, yes, kb + 3, smem + (kb % kStages) * kStage, kb + 1);   // O_kb
         end_o();
       }
       for (; kb < nkb; ++kb) {
         mfma();
+        scale_rows();
         end_e(kb);
         xphase(no, yes, 0, smem, min(kb + 1, nkb - 1));
         end_o();
@@ -457,18 +466,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
       xphase(no, no, 0, smem, 0);                                       // E_0
       end_e(0);
       mfma();                                                           // O_0
+      scale_rows();
       end_o();
       int kb = 1;
       for (; kb + 2 < nkb; ++kb) {
         xphase(yes, yes, kb + 2, smem + ((kb + 2) % kStages) * kStage, kb);   // E_kb
         end_e(kb);
         mfma();                                                         // O_kb
+        scale_rows();
         end_o();
       }
       for (; kb < nkb; ++kb) {
         xphase(no, yes, 0, smem, kb);
         end_e(kb);
         mfma();
+        scale_rows();
         end_o();
       }
       fma();
