@@ -11,6 +11,8 @@
 // Bias update (same page, section III "How the bias is set"; "DeepSeek-V3,
 // explained.", recipe step 4): overloaded experts lose gamma, underloaded ones
 // gain gamma, judged by an exact integer comparison of N * count with T * k.
+#include <type_traits>
+
 #include "common.h"
 
 namespace {
@@ -18,6 +20,13 @@ namespace {
 using namespace moe;
 
 constexpr int kCombineBlock = 256;
+
+// 16 bytes read once: a non-temporal load keeps them out of the caches' way
+__device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __global__ __launch_bounds__(kCombineBlock) void combine_kernel(
     const uint16_t* __restrict__ out, const float* __restrict__ gate,
@@ -27,61 +36,69 @@ __global__ __launch_bounds__(kCombineBlock) void combine_kernel(
   // of every block has work whatever H is
   const int chunks = H >> 3;
   const long long items = (long long)T * chunks;
-  for (long long item = (long long)blockIdx.x * kCombineBlock + threadIdx.x; item < items;
-       item += (long long)gridDim.x * kCombineBlock) {
-    const int t = (int)(item / chunks);
-    const int c8 = (int)(item - (long long)t * chunks);
-    float acc[8];
-    const long long col = (long long)c8 * 8;
-    uint4 base = make_uint4(0, 0, 0, 0);
-    if (shared_row0 >= 0)
-      base = *reinterpret_cast<const uint4*>(out + (long long)(shared_row0 + t) * H + col);
-    const uint32_t bw[4] = {base.x, base.y, base.z, base.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = bf16_lo(bw[i]);
-      acc[2 * i + 1] = bf16_hi(bw[i]);
-    }
-    if (residual) {
-      const uint4 r = *reinterpret_cast<const uint4*>(residual + (long long)t * H + col);
-      const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+  // When a row has a multiple of 64 chunks, a wave's 64 items share one token:
+  // that copy of the loop reads its slot rows and gates with scalar loads.
+  auto run = [&](auto uniform_c) {
+    constexpr bool UNIFORM = decltype(uniform_c)::value;
+    for (long long item = (long long)blockIdx.x * kCombineBlock + threadIdx.x; item < items;
+         item += (long long)gridDim.x * kCombineBlock) {
+      int t = (int)(item / chunks);
+      if (UNIFORM) t = __builtin_amdgcn_readfirstlane(t);
+      const int c8 = (int)(item - (long long)t * chunks);
+      float acc[8];
+      const long long col = (long long)c8 * 8;
+      uint4 base = make_uint4(0, 0, 0, 0);
+      if (shared_row0 >= 0)
+        base = load_stream(out + (long long)(shared_row0 + t) * H + col);
+      const uint32_t bw[4] = {base.x, base.y, base.z, base.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = bf16_lo(rw[i]) + acc[2 * i];
-        acc[2 * i + 1] = bf16_hi(rw[i]) + acc[2 * i + 1];
+        acc[2 * i] = bf16_lo(bw[i]);
+        acc[2 * i + 1] = bf16_hi(bw[i]);
       }
-    }
-    for (int j0 = 0; j0 < k; j0 += 8) {
-      const int jn = min(8, k - j0);
-      uint4 rows[8];
-      float g[8];
+      if (residual) {
+        const uint4 r = *reinterpret_cast<const uint4*>(residual + (long long)t * H + col);
+        const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < jn) {
-          const int r = row_of[(long long)t * k + j0 + j];
-          g[j] = gate[(long long)t * k + j0 + j];
-          rows[j] = *reinterpret_cast<const uint4*>(out + (long long)r * H + col);
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = bf16_lo(rw[i]) + acc[2 * i];
+          acc[2 * i + 1] = bf16_hi(rw[i]) + acc[2 * i + 1];
         }
       }
+      for (int j0 = 0; j0 < k; j0 += 8) {
+        const int jn = min(8, k - j0);
+        uint4 rows[8];
+        float g[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < jn) {
-          const uint32_t w[4] = {rows[j].x, rows[j].y, rows[j].z, rows[j].w};
+        for (int j = 0; j < 8; ++j) {
+          if (j < jn) {
+            const int r = row_of[(long long)t * k + j0 + j];
+            g[j] = gate[(long long)t * k + j0 + j];
+            rows[j] = load_stream(out + (long long)r * H + col);
+          }
+        }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[2 * i] = __builtin_fmaf(g[j], bf16_lo(w[i]), acc[2 * i]);
-            acc[2 * i + 1] = __builtin_fmaf(g[j], bf16_hi(w[i]), acc[2 * i + 1]);
+        for (int j = 0; j < 8; ++j) {
+          if (j < jn) {
+            const uint32_t w[4] = {rows[j].x, rows[j].y, rows[j].z, rows[j].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              acc[2 * i] = __builtin_fmaf(g[j], bf16_lo(w[i]), acc[2 * i]);
+              acc[2 * i + 1] = __builtin_fmaf(g[j], bf16_hi(w[i]), acc[2 * i + 1]);
+            }
           }
         }
       }
+      uint4 o;
+      o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+      o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+      o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
+      o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+      *reinterpret_cast<uint4*>(y + (long long)t * H + col) = o;
     }
-    uint4 o;
-    o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-    o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-    o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
-    o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
-    *reinterpret_cast<uint4*>(y + (long long)t * H + col) = o;
-  }
+  };
+  if ((chunks & 63) == 0) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 __global__ __launch_bounds__(256) void bias_update_kernel(float* __restrict__ bias,
