@@ -43,13 +43,35 @@ __device__ __forceinline__ uint32_t sortable(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// One step of a 64-bit maximum across lanes: (hi, lo) takes the DPP-moved
+// neighbour's pair when that pair is larger.
+template <int CTRL>
+__device__ __forceinline__ void dpp_max_step(uint32_t& hi, uint32_t& lo) {
+  const uint32_t oh = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, CTRL, 0xF, 0xF, false);
+  const uint32_t ol = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, CTRL, 0xF, 0xF, false);
+  const bool take = oh > hi || (oh == hi && ol > lo);
+  hi = take ? oh : hi;
+  lo = take ? ol : lo;
+}
+
+// Wave-wide maximum of a 64-bit value (uniform result): within each row of 16
+// lanes by DPP (swap neighbours, swap pairs, mirror the halves, mirror the
+// row), then the four row maxima read out to scalar registers and compared.
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+  uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+  dpp_max_step<0xB1>(hi, lo);
+  dpp_max_step<0x4E>(hi, lo);
+  dpp_max_step<0x141>(hi, lo);
+  dpp_max_step<0x140>(hi, lo);
+  unsigned long long best = 0ull;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const unsigned long long w = __shfl_xor(v, o, 64);
-    v = w > v ? w : v;
+  for (int r = 0; r < 4; ++r) {
+    const unsigned long long c =
+        ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
+        (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
+    best = c > best ? c : best;
   }
-  return v;
+  return best;
 }
 
 // k rounds of wave-wide argmax over keys held PER lane-slots per lane (expert
@@ -82,7 +104,7 @@ __device__ __forceinline__ void wave_topk(const float (&key)[PER], const float (
 #pragma unroll
     for (int s = 0; s < PER; ++s)
       if (s == slot) s_e = score[s];
-    s_e = __shfl(s_e, owner, 64);
+    s_e = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_e), owner));
     if (lane == owner) taken |= 1u << slot;
     sum = sum + s_e;
     if (lane == r) {
