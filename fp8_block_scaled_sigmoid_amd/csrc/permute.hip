@@ -73,10 +73,18 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict_
   const int e = threadIdx.x;
   int run = 0;
   if (e < N) {
-    for (int b = 0; b < n_blocks; ++b) {
-      const int c = blk_counts[(long long)b * N + e];
-      blk_counts[(long long)b * N + e] = run;  // becomes the block's base row
-      run += c;
+    // 16 block counts in flight at a time (the loads of one batch are issued
+    // before any base row of it is written back)
+    for (int b0 = 0; b0 < n_blocks; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        c[i] = b0 + i < n_blocks ? blk_counts[(long long)(b0 + i) * N + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (b0 + i < n_blocks) blk_counts[(long long)(b0 + i) * N + e] = run;  // the block's base row
+        run += c[i];
+      }
     }
     counts[e] = run;
   }
