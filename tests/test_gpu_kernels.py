@@ -426,7 +426,9 @@ def _int_codes(rng, shape, lim=4):
 
 
 @pytest.mark.parametrize("K,n_out,sizes,gather", [
+    (128, 256, [1, 200, 0, 77], True),          # one K block: the prologue alone
     (256, 256, [0, 1, 127, 128, 129, 300, 0], False),
+    (512, 256, [129, 40], False),               # four K blocks: one copy per wave group
     (384, 384, [3, 140, 0, 64], True),
     (7168, 512, [5, 0, 200], True),
     (2048, 7168, [130, 3], False),
