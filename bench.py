@@ -13,8 +13,13 @@ prefill size (T = 8192, H 7168, 256 routed experts top-8 + 1 shared, I 2048).
 Other workloads: decode (T = 512), skew (T = 32768, ten batches cycled, load
 max/mean reported), tiny, routing (T = 16384: router, top-k, permutation and
 bias update only), and backward (the FP8 Dgrad and Wgrad GEMMs of both expert
-GEMMs at the prefill shape, on synthetic upstream gradients).  The timed region is K steps with an event pair around
-every launch on the launch stream; per-kernel times are the means of those.
+GEMMs at the prefill shape, on synthetic upstream gradients).  The timed
+region is K steps with an event pair around every launch on the launch stream;
+per-kernel times are the means of those, and each step's time runs from its
+first launch to its last (the median is reported beside the mean).  A second
+pass of K steps, each after a write of --flush-mb MiB that evicts the caches,
+gives the flushed median.  Measured peaks are reported beside the published
+ones: a 2 GiB device copy and the library's FP8 MFMA rate probe.
 --router-fp8 swaps in the opt-in FP8 router (x quantised before routing); the
 routing workload also times the other router on the same batch and reports
 how many tokens both send to the same expert set.
@@ -72,6 +77,38 @@ def measured_traffic(workload):
         return None
 
 
+def measured_peaks(moe, torch, st):
+    """What the device reaches in practice, beside the published peaks: a
+    plain 2 GiB device-to-device copy (read + write bytes per second) and the
+    FP8 MFMA rate probe of the library (back-to-back 16x16x128 FP8 MFMAs, four
+    waves per SIMD, no memory traffic)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 1 << 31
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record(st)
+    torch.cuda.synchronize()
+    copy_ms = e0.elapsed_time(e1) / 5
+    del src, dst
+    blocks, iters = 256 * 4, 4000
+    sink, _ = moe.moe_probe_fp8_mfma(blocks, 8)
+    torch.cuda.synchronize()
+    e0.record(st)
+    _, flops = moe.moe_probe_fp8_mfma(blocks, iters, sink=sink)
+    e1.record(st)
+    torch.cuda.synchronize()
+    mfma_ms = e0.elapsed_time(e1)
+    return {"copy_bytes_read": n, "copy_bytes_written": n, "copy_ms": round(copy_ms, 4),
+            "copy_GBps_read_plus_write": round(2 * n / (copy_ms * 1e-3) / 1e9, 1),
+            "fp8_mfma_probe_ms": round(mfma_ms, 4),
+            "fp8_mfma_TFLOPs": round(flops / (mfma_ms * 1e-3) / 1e12, 1)}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,8 +121,11 @@ def parse():
                     help="the opt-in FP8 router (x quantised 1x128 first, Wr 128x128) in place "
                          "of the bf16 one")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also time a plain 2 GiB device copy (reference for the HBM "
-                         "byte counters and the measured copy bandwidth)")
+                    help="also report the 2 GiB device copy under its own key (the reference "
+                         "for the HBM byte counters; the copy itself always runs, as one of "
+                         "the measured peaks)")
+    ap.add_argument("--flush-mb", type=int, default=512,
+                    help="size of the write that precedes every step of the flushed pass")
     return ap.parse_args()
 
 
@@ -238,6 +278,7 @@ def bench_routing(args, w, moe, torch, gen, wr, bias, st):
     kern = {n: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1])
                               for i in range(args.steps)]))
             for j, n in enumerate(names)}
+    step_ms = [evs[i][0][0].elapsed_time(evs[i][-1][1]) for i in range(args.steps)]
     route_bytes = route_bytes_of(T, H, N, k, args.router_fp8)
     gbs = route_bytes / (kern["route"] * 1e-3) / 1e9
     # the other router on the same batch and bias (after the timed region):
@@ -252,6 +293,9 @@ def bench_routing(args, w, moe, torch, gen, wr, bias, st):
     main_route(idx)
     same = (idx.sort(dim=1).values == idx_other.sort(dim=1).values).all(dim=1)
     agree = float(same.float().mean().item())
+    other_ms = e0.elapsed_time(e1) / args.steps
+    peaks = measured_peaks(moe, torch, st)
+    copy_gbs = peaks["copy_GBps_read_plus_write"]
     res = {
         "metric": "MoE routing tokens/s (sigmoid router + biased top-k + permutation + bias "
                   "update) at V3 shape, 1 GPU",
@@ -272,8 +316,11 @@ def bench_routing(args, w, moe, torch, gen, wr, bias, st):
                      "kernel_avg_ms": round(kern["route"], 4),
                      "algorithmic_bytes_per_launch": route_bytes},
         "kernel_ms": {n: round(v, 4) for n, v in kern.items()},
+        "step_ms_median": round(float(np.median(step_ms)), 4),
+        "route_frac_measured_copy_peak": round(gbs / copy_gbs, 4),
+        "measured_peaks": peaks,
         "other_router": {"router": "bf16" if args.router_fp8 else "fp8",
-                         "route_ms": round(e0.elapsed_time(e1) / args.steps, 4),
+                         "route_ms": round(other_ms, 4),
                          "same_expert_set_fraction": round(agree, 4)},
     }
     if not args.no_cpu_baseline:
@@ -415,6 +462,10 @@ def bench_backward(args, w, moe, torch, gen, lay, st):
                          "GBps": round(b / (kern[n] * 1e-3) / 1e9, 1)} for n, (f, b) in work.items()},
         "weight_transpose_ms": round(t_transpose, 3),
     }
+    peaks = measured_peaks(moe, torch, st)
+    res["measured_peaks"] = peaks
+    res["gemm_frac_measured_mfma_peak"] = round(
+        gemm_flops / (gemm_ms * 1e-3) / 1e12 / peaks["fp8_mfma_TFLOPs"], 4)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_backward(w, R)
     print(json.dumps(res))
@@ -545,6 +596,22 @@ def main():
     per = {n: [evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(args.steps)]
            for j, n in enumerate(names)}
     kern = {n: float(np.mean(v)) for n, v in per.items()}
+    # each step's own time: from the first launch's start event to the last
+    # launch's end event
+    step_ms = [evs[i][0][0].elapsed_time(evs[i][-1][1]) for i in range(args.steps)]
+    # a second pass of K steps, each preceded by a write of flush_mb MiB (not
+    # timed) so that no step finds the previous step's data in the caches
+    flush = torch.empty(max(args.flush_mb, 1) << 20, dtype=torch.uint8, device=dev)
+    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        flush.fill_(i & 0xFF)
+        fev[i][0].record(st)
+        step()
+        fev[i][1].record(st)
+    torch.cuda.synchronize()
+    flushed_ms = [a.elapsed_time(b) for a, b in fev]
+    del flush
     # after the timed region: the per-expert load max/mean of the workload's
     # batches (one more pass over them, each followed by a read of the counts)
     load_ratio = []
@@ -600,6 +667,9 @@ def main():
                   "hbm_frac": round(b / (kern[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
               for n, b in phase_bytes.items()}
 
+    peaks = measured_peaks(moe, torch, st)
+    for ph in phases.values():
+        ph["frac_measured_copy_peak"] = round(ph["GBps"] / peaks["copy_GBps_read_plus_write"], 4)
     res = {
         "metric": "MoE layer tokens/s + grouped FP8 GEMM TFLOP/s (% peak) at V3 shape, 1 GPU",
         "value": round(tokens_per_s, 1),
@@ -621,6 +691,11 @@ def main():
         "roofline": roof,
         "gemm_tflops": round(gemm_tflops, 2),
         "gemm_frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
+        "gemm_frac_measured_mfma_peak": round(gemm_tflops / peaks["fp8_mfma_TFLOPs"], 4),
+        "layer_ms_median": round(float(np.median(step_ms)), 4),
+        "layer_ms_median_flushed": round(float(np.median(flushed_ms)), 4),
+        "flush_mb": args.flush_mb,
+        "measured_peaks": peaks,
         "kernel_ms": {n: round(v, 4) for n, v in kern.items()},
         "hbm_phases": phases,
         "expert_load_max_over_mean": load_ratio if w.batches > 1 else load_ratio[-1],
@@ -628,20 +703,10 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
     if args.copy_calibration:
-        n = 1 << 31
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        e0.record(st)
-        for _ in range(5):
-            dst.copy_(src)
-        e1.record(st)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / 5
-        res["copy_calibration"] = {"bytes_read": n, "bytes_written": n, "ms": round(ms, 4),
-                                   "GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}
-        del src, dst
+        res["copy_calibration"] = {"bytes_read": peaks["copy_bytes_read"],
+                                   "bytes_written": peaks["copy_bytes_written"],
+                                   "ms": peaks["copy_ms"],
+                                   "GBps_read_plus_write": peaks["copy_GBps_read_plus_write"]}
     if not args.no_cpu_baseline and w.with_experts:
         res["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(res))

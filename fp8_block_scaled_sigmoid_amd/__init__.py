@@ -70,6 +70,7 @@ def lib():
             "fp8_transpose_128x128": [_P, _P, _I, _I, _I, _P, _P, _P],
             "fp8_quant_tokens_128": [_P, _I, _I, _I, _LL, _P, _I, _P, _P, _LL, _P, _P],
             "moe_grouped_wgrad_fp8": [_P, _P, _LL, _I, _P, _P, _LL, _I, _P, _I, _P, _P],
+            "moe_probe_fp8_mfma": [_I, _I, _P, _P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -364,6 +365,17 @@ def moe_seq_balance_loss(idx, gate, seq_offsets, n_experts, alpha=1e-4, loss=Non
         _ptr(idx), _ptr(gate), _ptr(seq_offsets), S, T, n_experts, k, alpha, _ptr(loss),
         _stream(stream)))
     return loss
+
+
+def moe_probe_fp8_mfma(blocks, iters, sink=None, stream=None):
+    """Enqueue the FP8 MFMA rate probe (a diagnostic, not a layer step):
+    blocks * 4 waves, each issuing iters * 16 16x16x128 FP8 MFMAs.  Returns
+    (sink, flops)."""
+    if sink is None:
+        sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    _check("moe_probe_fp8_mfma", lib().moe_probe_fp8_mfma(blocks, iters, _ptr(sink),
+                                                          _stream(stream)))
+    return sink, float(blocks) * 4 * iters * 16 * 65536
 
 
 # ---------------------------------------------------------------------------

@@ -318,6 +318,18 @@ moe_status_t moe_grouped_wgrad_fp8(const uint8_t* a_q, const float* a_d, long lo
                                    long long ldb, int k_rows, const int32_t* pad_offsets,
                                    int num_groups, float* out, hipStream_t stream);
 
+/*
+ * Diagnostic, not a step of the layer: the attainable rate of the FP8 matrix
+ * instruction the grouped GEMMs use (v_mfma_f32_16x16x128_f8f6f4), so that a
+ * GEMM's throughput can be stated against a measured peak beside the published
+ * one.  Enqueues `blocks` workgroups of 4 waves; every wave issues
+ * iters * 16 of these MFMAs (16 independent accumulators, no memory traffic
+ * in the loop), i.e. blocks * 4 * iters * 16 * 65536 flops in all, and writes
+ * blocks * 256 floats to `sink` (device, caller-owned).  The caller times it
+ * (events on `stream`).  1 <= blocks <= 2^20, iters >= 1 (MOE_ERR_SHAPE).
+ */
+moe_status_t moe_probe_fp8_mfma(int blocks, int iters, float* sink, hipStream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char* moe_status_str(moe_status_t status);
 /* hipError_t of the most recent MOE_ERR_HIP on this thread (0 if none). */

@@ -125,6 +125,11 @@ def test_validation_before_any_launch(lib):
     assert lib.moe_grouped_wgrad_fp8(None, None, 200, 128, None, None, 256, 128, None, 2, None, None) == 2
     assert lib.moe_grouped_wgrad_fp8(None, None, 256, 128, None, None, 256, 128, None, 2, None, None) == 1
     assert lib.moe_grouped_wgrad_fp8(None, None, 256, 0, None, None, 256, 128, None, 2, None, None) == 0
+    # the MFMA rate probe: shape first, then the sink pointer
+    lib.moe_probe_fp8_mfma.argtypes = [I, I, P, P]
+    assert lib.moe_probe_fp8_mfma(0, 10, None, None) == 2
+    assert lib.moe_probe_fp8_mfma(4, 0, None, None) == 2
+    assert lib.moe_probe_fp8_mfma(4, 10, None, None) == 1
     lib.moe_permute_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_permute_workspace_bytes.argtypes = [I, I, I]
     assert lib.moe_permute_workspace_bytes(513, 256, 8) == 3 * 256 * 4

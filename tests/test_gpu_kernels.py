@@ -682,3 +682,20 @@ def test_seq_balance_loss_against_oracle():
     np.testing.assert_allclose(got, want, rtol=1e-6, atol=0)
     assert got[2] == 0.0
     assert np.array_equal(got, loss2.cpu().numpy())
+
+
+# --------------------------------------------------------------------------- diagnostics
+
+
+def test_mfma_rate_probe_runs():
+    """The FP8 MFMA rate probe (a diagnostic the benchmark times): finite,
+    positive sums from finite codes, identical on a second call."""
+    moe = _moe()
+    log("moe_probe_fp8_mfma")
+    sink, flops = moe.moe_probe_fp8_mfma(8, 3)
+    again, _ = moe.moe_probe_fp8_mfma(8, 3)
+    torch.cuda.synchronize()
+    assert flops == 8 * 4 * 3 * 16 * 65536
+    s = sink.cpu().numpy()
+    assert np.all(np.isfinite(s)) and np.all(s > 0)
+    assert np.array_equal(s, again.cpu().numpy())
