@@ -430,6 +430,7 @@ def _int_codes(rng, shape, lim=4):
     (256, 256, [0, 1, 127, 128, 129, 300, 0], False),
     (512, 256, [129, 40], False),               # four K blocks: one copy per wave group
     (384, 384, [3, 140, 0, 64], True),
+    (256, 384, [20, 64, 192, 100, 33], True),   # tails of 20, 64 and 33 rows: narrow tiles
     (7168, 512, [5, 0, 200], True),
     (2048, 7168, [130, 3], False),
 ])
@@ -501,7 +502,7 @@ def _swiglu_case(integer):
     moe = _moe()
     rng = np.random.default_rng(12)
     H, I = 512, 256
-    sizes = [40, 0, 130, 7]
+    sizes = [40, 0, 130, 7, 64, 20, 192]
     off = _ragged_offsets(sizes)
     R, G = int(off[-1]), len(sizes)
     T = 50
