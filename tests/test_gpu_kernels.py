@@ -147,7 +147,8 @@ def test_quant_128x128_bit_exact(interleave):
 
 @pytest.mark.parametrize("T,N,k,ties", [(1000, 16, 2, False), (777, 256, 8, False),
                                         (500, 256, 8, True), (64, 1000, 32, False),
-                                        (300, 32, 32, False), (129, 48, 1, True)])
+                                        (300, 32, 32, False), (129, 48, 1, True),
+                                        (200, 1024, 32, True)])   # the largest N and k
 def test_topk_from_scores_bit_exact(T, N, k, ties):
     moe = _moe()
     rng = np.random.default_rng(T + N + k)
@@ -397,7 +398,8 @@ def test_route_topk_grouped_v3_shape():
 @pytest.mark.parametrize("T,N,k,shared", [(1, 16, 1, True), (255, 16, 2, True),
                                           (256, 256, 8, True), (257, 256, 8, False),
                                           (4097, 1000, 8, True), (3000, 64, 32, True),
-                                          (16384, 256, 8, True)])
+                                          (16384, 256, 8, True),
+                                          (600, 1024, 32, True)])   # the largest N and k
 def test_permute_bit_exact(T, N, k, shared):
     moe = _moe()
     rng = np.random.default_rng(T * 7 + N)
@@ -433,6 +435,7 @@ def _int_codes(rng, shape, lim=4):
     (256, 384, [20, 64, 192, 100, 33], True),   # tails of 20, 64 and 33 rows: narrow tiles
     (7168, 512, [5, 0, 200], True),
     (2048, 7168, [130, 3], False),
+    (16384, 256, [3, 130], True),               # the largest K: 128 K blocks
 ])
 def test_gemm_integer_operands_bit_exact(K, n_out, sizes, gather):
     """Integer-valued codes with power-of-two scales: every partial sum is an
@@ -462,6 +465,35 @@ def test_gemm_integer_operands_bit_exact(K, n_out, sizes, gather):
         got = out.float().cpu().numpy().astype(np.float64)
         ref = want if epi == moe.MOE_EPI_F32 else ffn.bf16_round(want)
         assert np.array_equal(got, ref)
+
+
+def test_gemm_many_groups_bit_exact():
+    """1025 groups (the most the tile scan takes, three per thread), most of
+    them empty, the others of 1 to 140 rows, integer operands: bit-exact."""
+    moe = _moe()
+    rng = np.random.default_rng(1025)
+    G, K, n_out = 1025, 256, 256
+    sizes = np.zeros(G, np.int64)
+    live = rng.choice(G, 40, replace=False)
+    sizes[live] = rng.integers(1, 141, live.size)
+    sizes[G - 1] = 129                      # the last group: a one-row tail
+    off = _ragged_offsets(sizes)
+    R = int(off[-1])
+    aq = _int_codes(rng, (R, K))
+    ad = np.full((R, K // 128), 2.0 ** -2, np.float32)
+    bq = np.zeros((G, n_out, K), np.uint8)
+    bd = np.full((G, n_out // 128, K // 128), 2.0 ** -4, np.float32)
+    for g in np.nonzero(sizes)[0]:
+        bq[g] = _int_codes(rng, (n_out, K))
+    want = np.zeros((R, n_out))
+    for g in np.nonzero(sizes)[0]:
+        rr = np.arange(off[g], off[g + 1])
+        want[rr] = ffn.block_scaled_gemm(aq[rr], ad[rr], bq[g], bd[g])
+    log("moe_grouped_gemm_fp8 1025 groups")
+    out, _ = moe.moe_grouped_gemm_fp8(to_dev(aq), to_dev(ad), to_dev(bq), to_dev(bd),
+                                      to_dev(off), R, moe.MOE_EPI_F32)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), want)
 
 
 def _random_codes(rng, shape):
