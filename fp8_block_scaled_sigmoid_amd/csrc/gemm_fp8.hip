@@ -263,10 +263,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     if (i < 2) dma16(rs_a, a_off[i], ko, st + (8 * i + wave) * 1024);
     else dma16(rs_b, b_off[i - 2], ko, st + kABytes + (8 * (i - 2) + wave) * 1024);
   };
-  auto issue = [&](int kb, uint8_t* st) {
-#pragma unroll
-    for (int part = 0; part < 4; ++part) issue_part(kb, st, part);
-  };
 
   // ---- wave tile: rows wm*64..+64, B-tile rows wn*64..+64; wn < 2 lies in
   // weight block 0 (gate), wn >= 2 in block 1 (up)
@@ -370,7 +366,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 #pragma unroll
       for (int q = 0; q < 4 * NMI; ++q) {
         if (q < q0 || q >= q1) continue;
-        const int ni = q / NMI, mi = q - ni * NMI;
+        const int ni = q / (NMI > 0 ? NMI : 1), mi = q - ni * NMI;
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           acc[mi][ni][v] = __builtin_fmaf(part[ni][mi][v], sc[mi][v], acc[mi][ni][v]);
