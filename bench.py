@@ -18,8 +18,9 @@ region is K steps with an event pair around every launch on the launch stream;
 per-kernel times are the means of those, and each step's time runs from its
 first launch to its last (the median is reported beside the mean).  A second
 pass of K steps, each after a write of --flush-mb MiB that evicts the caches,
-gives the flushed median.  Measured peaks are reported beside the published
-ones: a 2 GiB device copy and the library's FP8 MFMA rate probe.
+gives the flushed median, and K replays of one step captured in a HIP graph
+the graph step time.  Measured peaks are reported beside the published ones:
+a 2 GiB device copy and the library's FP8 MFMA rate probe.
 --router-fp8 swaps in the opt-in FP8 router (x quantised before routing); the
 routing workload also times the other router on the same batch and reports
 how many tokens both send to the same expert set.
@@ -612,6 +613,26 @@ def main():
     torch.cuda.synchronize()
     flushed_ms = [a.elapsed_time(b) for a, b in fev]
     del flush
+    # one step captured in a HIP graph and replayed K times (the launches of a
+    # step without their host-side cost); the captured step keeps the batch it
+    # was captured with
+    graph_ms = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(args.steps):
+            g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / args.steps
+        del g
+    except RuntimeError as err:      # reported, not fatal: the eager numbers stand
+        graph_ms = f"capture failed: {err}"
     # after the timed region: the per-expert load max/mean of the workload's
     # batches (one more pass over them, each followed by a read of the counts)
     load_ratio = []
@@ -694,6 +715,7 @@ def main():
         "gemm_frac_measured_mfma_peak": round(gemm_tflops / peaks["fp8_mfma_TFLOPs"], 4),
         "layer_ms_median": round(float(np.median(step_ms)), 4),
         "layer_ms_median_flushed": round(float(np.median(flushed_ms)), 4),
+        "graph_ms_per_step": round(graph_ms, 4) if isinstance(graph_ms, float) else graph_ms,
         "flush_mb": args.flush_mb,
         "measured_peaks": peaks,
         "kernel_ms": {n: round(v, 4) for n, v in kern.items()},

@@ -426,3 +426,47 @@ def test_gemm2_combine_rounding_faithful(T, H, N, k, I):
     err = rel_l2(bf16_values(y), want_y)
     print(f"rel L2: expert rows {err_out:.3e}, y {err:.3e}")
     assert err_out <= Q_BAR and err <= Q_BAR
+
+
+@pytest.mark.parametrize("router_fp8", [False, True])
+def test_layer_forward_graph_replay(router_fp8):
+    """MoELayer.forward allocates nothing, clears nothing with a memset and
+    syncs nothing, so one step can be captured in a HIP graph and replayed.
+    Four replays, each on a new batch copied into the graph's input buffer
+    (eager work and a synchronisation between replays), every one bit-exact
+    against a twin layer run eagerly on the same batches -- output, routing,
+    maps and the bias each step updates."""
+    moe = _moe()
+    w = synth.Workload("graph", T=300, H=512, N=128 if router_fp8 else 32, k=4, I=256, x_std=1.0,
+                       wr_dist=synth.NORMAL, wr_param=0.05, bias_half=0.1, w_std=0.02, seed=7)
+    wr = bf16_to_dev(w.router_weight())
+    w1 = bf16_to_dev(synth.generate(w.w1_spec(), w.seed))
+    w2 = bf16_to_dev(synth.generate(w.w2_spec(), w.seed))
+    b0 = to_dev(w.bias().copy())
+    layers = []
+    for _ in range(2):
+        weights = moe.MoEWeights(wr, b0.clone(), w1_bf16=w1, w2_bf16=w2, router_fp8=router_fp8)
+        layers.append(moe.MoELayer(weights, w.T, w.k, w.gamma, router_fp8=router_fp8))
+    eager, graphed = layers
+    xs = [bf16_to_dev(synth.generate(w.x_spec(b), w.seed)) for b in range(4)]
+    log(f"graph capture of MoELayer.forward router_fp8={router_fp8}")
+    x_static = torch.empty_like(xs[0])
+    x_static.copy_(xs[0])
+    graphed.forward(x_static, update_bias=False)      # first launches outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        y_static = graphed.forward(x_static)
+    torch.cuda.synchronize()
+    graphed.w.bias.copy_(b0)                           # the capture itself ran nothing
+    for b, x in enumerate(xs):
+        y_e = eager.forward(x).clone()
+        torch.cuda.synchronize()
+        x_static.copy_(x)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_static, y_e), f"replay {b}: output differs"
+        assert torch.equal(graphed.idx, eager.idx), f"replay {b}: routing differs"
+        assert torch.equal(graphed.token_of, eager.token_of), f"replay {b}: row map differs"
+        assert torch.equal(graphed.w.bias, eager.w.bias), f"replay {b}: bias differs"
+    assert not torch.equal(eager.w.bias, b0)           # the bias did move
