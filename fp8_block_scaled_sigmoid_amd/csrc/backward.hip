@@ -426,13 +426,10 @@ extern "C" moe_status_t moe_grouped_wgrad_fp8(const uint8_t* a_q, const float* a
       (reinterpret_cast<uintptr_t>(a_d) & 3) || (reinterpret_cast<uintptr_t>(b_d) & 3))
     return MOE_ERR_ALIGN;
   if (moe_status_t s = check_device()) return s;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kWLds);
-    if (e != hipSuccess) return hip_fail(e);
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (moe_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(&wgrad_kernel),
+                                          kWLds, lds_set))
+    return st;
   WgradParams p;
   p.a_q = a_q; p.a_d = a_d; p.lda = lda; p.b_q = b_q; p.b_d = b_d; p.ldb = ldb;
   p.pad = pad_offsets; p.G = num_groups; p.N = n_rows; p.K = k_rows; p.out = out;

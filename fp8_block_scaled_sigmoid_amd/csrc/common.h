@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "moe_fp8.h"
 
 #ifndef __HIP_DEVICE_COMPILE__
@@ -78,5 +80,11 @@ moe_status_t hip_fail(hipError_t e);          // records e, returns MOE_ERR_HIP
 moe_status_t launch_status();                 // hipGetLastError -> status
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Lets kernel `func` use `bytes` of dynamic LDS on the current device.  The
+// attribute is set once per (launch site, device): `done` is the launch site's
+// mask of devices already set (bit d for device d < 64; devices beyond 63 are
+// set on every call).  Safe to call from several host threads at once.
+moe_status_t allow_dynamic_lds(const void* func, int bytes, std::atomic<uint64_t>& done);
 
 }  // namespace moe

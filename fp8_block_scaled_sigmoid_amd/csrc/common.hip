@@ -27,6 +27,18 @@ moe_status_t check_device() {
   return state == 1 ? MOE_OK : MOE_ERR_DEVICE;
 }
 
+moe_status_t allow_dynamic_lds(const void* func, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return MOE_OK;
+  e = hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return hip_fail(e);
+  if (bit) done.fetch_or(bit, std::memory_order_release);
+  return MOE_OK;
+}
+
 moe_status_t hip_fail(hipError_t e) {
   g_last_hip_error = static_cast<int>(e);
   return MOE_ERR_HIP;

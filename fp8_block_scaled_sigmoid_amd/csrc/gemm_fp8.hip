@@ -612,13 +612,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 
 template <int EPI>
 moe_status_t launch(const GemmParams& p, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_kernel<EPI>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (e != hipSuccess) return hip_fail(e);
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (moe_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(&grouped_gemm_kernel<EPI>),
+                                          kLds, lds_set))
+    return st;
   const long long n_tiles = (p.n_out + BN - 1) / BN;
   long long grid = ((long long)(p.total_rows + BM - 1) / BM + p.G) * n_tiles;
   grid = (grid + 7) / 8 * 8;

@@ -550,13 +550,10 @@ extern "C" moe_status_t moe_route_topk(const void* x_bf16, const void* w_router_
   if (!ws || ws_bytes < moe_route_workspace_bytes(T, H, N)) return MOE_ERR_WORKSPACE;
   if (!aligned16(x_bf16) || !aligned16(w_router_bf16) || !aligned16(ws)) return MOE_ERR_ALIGN;
   if (moe_status_t st = check_device()) return st;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_partial_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kRLds);
-    if (e != hipSuccess) return hip_fail(e);
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (moe_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(&route_partial_kernel),
+                                          kRLds, lds_set))
+    return st;
   const int S = route_splits(T, H);
   const int tiles = (T + kRT - 1) / kRT;
   const int grid = (tiles * S + 7) / 8 * 8;
@@ -598,13 +595,10 @@ extern "C" moe_status_t moe_route_topk_fp8(const uint8_t* x_q, const float* x_d,
       (reinterpret_cast<uintptr_t>(x_d) & 3) || (reinterpret_cast<uintptr_t>(w_router_d) & 3))
     return MOE_ERR_ALIGN;
   if (moe_status_t st = check_device()) return st;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_partial_fp8_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kRLdsF);
-    if (e != hipSuccess) return hip_fail(e);
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (moe_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(&route_partial_fp8_kernel),
+                                          kRLdsF, lds_set))
+    return st;
   const int S = route_splits(T, H / 2);   // one chunk here is 128 codes, not 64
   const int tiles = (T + kRT - 1) / kRT;
   const int grid = (tiles * S + 7) / 8 * 8;
