@@ -35,13 +35,20 @@
 //     wave and its up partner swap half of their subtiles through LDS so all
 //     8 waves form h, and the 128 h columns of a row (one 1x128 quantisation
 //     tile) meet in LDS for the tile maximum;
+//   * two K-loop schedules, chosen by the epilogue at compile time (each was
+//     measured faster for its case): with the SwiGLU epilogue (GEMM1) the
+//     "ping-pong" loop, two wave groups alternating MFMA and VALU/memory
+//     phases; with the bf16 and float32 epilogues (GEMM2, Dgrad) the
+//     single-group loop, and a workgroup computes two adjacent column tiles of
+//     the same rows one after the other, the second reusing the group lookup
+//     and the row map;
 //   * every workgroup derives the tile list itself from the device-side group
-//     offsets (tiles ordered group, column tile, row tile), so the call needs no
-//     workspace and no host sync; consecutive row tiles of one (expert, column
-//     tile) are mapped to the same XCD so their weight tile is fetched from HBM
-//     once and re-read from that XCD's L2; in a group's last row tile, 16-row
-//     subtiles past the group's end skip their MFMAs (the K loop is compiled
-//     for each count of live subtiles).
+//     offsets (tiles ordered group, column tile (or pair), row tile), so the
+//     call needs no workspace and no host sync; consecutive row tiles of one
+//     (expert, column tile) are mapped to the same XCD so their weight tile is
+//     fetched from HBM once and re-read from that XCD's L2; in a group's last
+//     row tile, 16-row subtiles past the group's end skip their MFMAs (the K
+//     loop is compiled for each count of live subtiles).
 #include <type_traits>
 
 #include "common.h"
@@ -132,6 +139,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.G;
   const int n_tiles = (p.n_out + BN - 1) / BN;   // the last tile may be 128 wide
+  // the SwiGLU epilogue runs the ping-pong K loop on one column tile; the
+  // others run the single-group K loop on two adjacent column tiles of the
+  // same rows, one after the other (the second reuses the group lookup and
+  // the row map, so it starts with its copies)
+  constexpr bool kPingPong = EPI == MOE_EPI_SWIGLU_FP8;
+  constexpr int kPer = kPingPong ? 1 : 2;
+  const int n_cols = (n_tiles + kPer - 1) / kPer;
 
   // ---- tile list: tiles are ordered (group, column tile, row tile), and
   // group g owns ceil(rows_g / BM) * n_tiles of them.  Thread t counts the
@@ -152,7 +166,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
         const int r0 = clampi(p.offsets[gi], 0, p.total_rows);
         const int r1 = clampi(p.offsets[gi + 1], 0, p.total_rows);
         const int rows = r1 > r0 ? r1 - r0 : 0;
-        c = ((rows + BM - 1) / BM) * n_tiles;
+        c = ((rows + BM - 1) / BM) * n_cols;
       }
       cnt[i] = c;
       run += c;
@@ -195,18 +209,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   const int row0 = clampi(p.offsets[g], 0, p.total_rows);
   const int rows_g = clampi(p.offsets[g + 1], 0, p.total_rows) - row0;
   const int mt = (rows_g + BM - 1) / BM;
-  const int n_tile = local / mt;
-  const int m0 = (local - n_tile * mt) * BM;
+  const int col = local / mt;                           // column tile (or pair)
+  const int m0 = (local - col * mt) * BM;
   const int rows_valid = min(BM, rows_g - m0);
   const int nkb = p.k_dim / BK;
-  const bool half_tile = p.n_out - n_tile * BN < BN;   // only 128 columns exist
-
-  // B scales of both weight blocks of this tile, for every K block
-  for (int i = tid; i < 2 * nkb; i += kThreads) {
-    const int blk = i / nkb, kb = i - blk * nkb;
-    const int nb = min(2 * n_tile + blk, p.n_out / 128 - 1);
-    s_bd[blk][kb] = p.b_d[((long long)g * (p.n_out / 128) + nb) * nkb + kb];
-  }
+  const int n_here = min(kPer, n_tiles - kPer * col);   // column tiles of this workgroup
 
   // ---- direct-to-LDS sources.  Load j of wave w writes 1 KiB block
   // b = 8 j + w (rows 8 b .. 8 b + 7); lane l fills row 8 b + (l >> 3) at chunk
@@ -232,6 +239,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     src = clampi(src, 0, p.a_rows - 1);
     sa_off = src * nkb_all * 4;
   }
+#pragma unroll
+  for (int hh = 0; hh < kPer; ++hh) {
+  if (hh >= n_here) break;
+  const int n_tile = kPer * col + hh;
+  const bool half_tile = p.n_out - n_tile * BN < BN;   // only 128 columns exist
+  if (hh > 0) __syncthreads();   // the previous tile's epilogue is done with LDS
+
+  // B scales of both weight blocks of this tile, for every K block
+  for (int i = tid; i < 2 * nkb; i += kThreads) {
+    const int blk = i / nkb, kb = i - blk * nkb;
+    const int nb = min(2 * n_tile + blk, p.n_out / 128 - 1);
+    s_bd[blk][kb] = p.b_d[((long long)g * (p.n_out / 128) + nb) * nkb + kb];
+  }
   const int b_rows = half_tile ? 128 : BN;
   const __amdgpu_buffer_rsrc_t rs_b =
       make_rsrc(p.b_q + ((long long)g * p.n_out + (long long)n_tile * BN) * p.k_dim, b_rows * p.k_dim);
@@ -256,6 +276,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     } else if (wave < 2) {
       dma4(rs_sa, sa_off, kb * 4, st + kABytes + kBBytes + wave * 256);
     }
+  };
+  auto issue = [&](int kb, uint8_t* st) {
+#pragma unroll
+    for (int part = 0; part < 4; ++part) issue_part(kb, st, part);
   };
   // copy i (0-5) of this wave's A and B share of a stage: A loads 0-1, B loads 0-3
   auto issue_one = [&](int kb, uint8_t* st, int i) {
@@ -482,13 +506,113 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
       fma();
     }
   };
+  // The single-group K loop (bf16 and float32 epilogues): every wave runs
+  // every K block; after one barrier per block it reads its fragments, and
+  // for each column subtile issues the 4 MFMAs while the scale FMAs of the
+  // previous subtile and one part of the copies of stage kb + 2 run behind
+  // them.
+  auto kloop_sg = [&](auto nmi_c) {
+    constexpr int NMI = decltype(nmi_c)::value;
+    // one K block.  MORE: stage kb + 2 exists and is requested meanwhile;
+    // LAST: no stage follows this one.
+    auto kblock = [&](int kb, auto more_c, auto last_c) {
+      constexpr bool more = decltype(more_c)::value, last = decltype(last_c)::value;
+      // stage kb must have landed; stage kb + 1 may still be in flight
+      if (!last) {
+        if (wave < 2) wait_and_barrier<7>(); else wait_and_barrier<6>();
+      } else {
+        wait_and_barrier<0>();
+      }
+      uint8_t* st_next = smem + ((kb + 2) % kStages) * kStage;
+      if (NMI == 0) {
+        if (more) issue(kb + 2, st_next);
+        return;
+      }
+      // MFMA lane group lk takes the 16-byte K chunks lk and lk + 4 of its
+      // row, for A and B alike (a fixed permutation of K inside the block,
+      // so the dot product is unchanged); this keeps each ds_read_b128 free
+      // of LDS bank conflicts, which chunks 2 lk and 2 lk + 1 are not.
+      // The A fragments, row scales and the first B fragment are read first;
+      // then for each column subtile ni: the next B fragment is read and one
+      // part of stage kb + 2 is requested while the 4 MFMAs of ni run, with
+      // the scale FMAs of subtile ni - 1 behind them (no FMA waits on a
+      // fresh result).
+      // Subtile rows differ by multiples of 16, so a lane's swizzle term is
+      // the same in every subtile: one lane offset per chunk half, and the
+      // subtiles sit at constant offsets from it.
+      const uint8_t* st = smem + (kb % kStages) * kStage;
+      const float* sA = reinterpret_cast<const float*>(st + kABytes + kBBytes) + wm * 64 + 4 * lk;
+      const float sb = s_bd[wn >> 1][kb];
+      const uint8_t* a_lo = st + wm * 64 * 128 + frag_lo;
+      const uint8_t* a_hi = st + wm * 64 * 128 + frag_hi;
+      const uint8_t* b_lo = st + kABytes + wn * 64 * 128 + frag_lo;
+      const uint8_t* b_hi = st + kABytes + wn * 64 * 128 + frag_hi;
+      auto read_b = [&](int ni) {
+        const i32x4 y0 = *reinterpret_cast<const i32x4*>(b_lo + ni * 16 * 128);
+        const i32x4 y1 = *reinterpret_cast<const i32x4*>(b_hi + ni * 16 * 128);
+        return __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      // read order = use order: A0 and B0 first, so the first MFMA waits for
+      // four reads only, then the other A fragments, then the row scales
+      // (first needed by the FMAs behind the second column subtile)
+      f32x4 sc[4];
+      i32x8 af[4], bfr[2];
+      auto read_a = [&](int mi) {
+        const i32x4 x0 = *reinterpret_cast<const i32x4*>(a_lo + mi * 16 * 128);
+        const i32x4 x1 = *reinterpret_cast<const i32x4*>(a_hi + mi * 16 * 128);
+        return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      af[0] = read_a(0);
+      bfr[0] = read_b(0);
+#pragma unroll
+      for (int mi = 1; mi < NMI; ++mi) af[mi] = read_a(mi);
+#pragma unroll
+      for (int mi = 0; mi < NMI; ++mi) sc[mi] = *reinterpret_cast<const f32x4*>(sA + mi * 16);
+#pragma unroll
+      for (int mi = 0; mi < NMI; ++mi) sc[mi] = sc[mi] * sb;
+      f32x4 part[2][4];
+#pragma unroll
+      for (int ni = 0; ni < 5; ++ni) {
+        if (ni < 3) bfr[(ni + 1) & 1] = read_b(ni + 1);
+        if (ni < 4 && more) issue_part(kb + 2, st_next, ni);
+#pragma unroll
+        for (int mi = 0; mi < NMI; ++mi) {
+          if (ni < 4)
+            part[ni & 1][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                af[mi], bfr[ni & 1], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+          if (ni > 0) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              acc[mi][ni - 1][v] =
+                  __builtin_fmaf(part[(ni - 1) & 1][mi][v], sc[mi][v], acc[mi][ni - 1][v]);
+          }
+        }
+      }
+    };
+    issue(0, smem);
+    if (nkb > 1) issue(1, smem + kStage);
+    int kb = 0;
+    for (; kb + 2 < nkb; ++kb) kblock(kb, std::true_type{}, std::false_type{});
+    if (kb + 1 < nkb) kblock(kb++, std::false_type{}, std::false_type{});
+    kblock(kb, std::false_type{}, std::true_type{});
+  };
   const int nmi = wave_cols ? clampi((wave_rows + 15) >> 4, 0, 4) : 0;
-  switch (__builtin_amdgcn_readfirstlane(nmi)) {
-    case 4: kloop(std::integral_constant<int, 4>{}); break;
-    case 3: kloop(std::integral_constant<int, 3>{}); break;
-    case 2: kloop(std::integral_constant<int, 2>{}); break;
-    case 1: kloop(std::integral_constant<int, 1>{}); break;
-    default: kloop(std::integral_constant<int, 0>{}); break;
+  if constexpr (kPingPong) {
+    switch (__builtin_amdgcn_readfirstlane(nmi)) {
+      case 4: kloop(std::integral_constant<int, 4>{}); break;
+      case 3: kloop(std::integral_constant<int, 3>{}); break;
+      case 2: kloop(std::integral_constant<int, 2>{}); break;
+      case 1: kloop(std::integral_constant<int, 1>{}); break;
+      default: kloop(std::integral_constant<int, 0>{}); break;
+    }
+  } else {
+    switch (__builtin_amdgcn_readfirstlane(nmi)) {
+      case 4: kloop_sg(std::integral_constant<int, 4>{}); break;
+      case 3: kloop_sg(std::integral_constant<int, 3>{}); break;
+      case 2: kloop_sg(std::integral_constant<int, 2>{}); break;
+      case 1: kloop_sg(std::integral_constant<int, 1>{}); break;
+      default: kloop_sg(std::integral_constant<int, 0>{}); break;
+    }
   }
   __syncthreads();   // every wave is done with the stages before they are reused
 
@@ -608,6 +732,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
         }
       }
   }
+
+  }
 }
 
 template <int EPI>
@@ -616,8 +742,9 @@ moe_status_t launch(const GemmParams& p, hipStream_t stream) {
   if (moe_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(&grouped_gemm_kernel<EPI>),
                                           kLds, lds_set))
     return st;
-  const long long n_tiles = (p.n_out + BN - 1) / BN;
-  long long grid = ((long long)(p.total_rows + BM - 1) / BM + p.G) * n_tiles;
+  constexpr long long per = EPI == MOE_EPI_SWIGLU_FP8 ? 1 : 2;   // column tiles per workgroup
+  const long long n_cols = ((p.n_out + BN - 1) / BN + per - 1) / per;
+  long long grid = ((long long)(p.total_rows + BM - 1) / BM + p.G) * n_cols;
   grid = (grid + 7) / 8 * 8;
   if (grid > 0x7FFFFFFFLL) return MOE_ERR_SHAPE;
   hipLaunchKernelGGL(grouped_gemm_kernel<EPI>, dim3((unsigned)grid), dim3(kThreads), kLds, stream, p);
