@@ -78,6 +78,7 @@ namespace moe {
 moe_status_t check_device();                  // MOE_ERR_DEVICE unless gfx950
 moe_status_t hip_fail(hipError_t e);          // records e, returns MOE_ERR_HIP
 moe_status_t launch_status();                 // hipGetLastError -> status
+int cu_count();                               // compute units of the current device (0 on error)
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -7,6 +7,7 @@ namespace {
 thread_local int g_last_hip_error = 0;
 constexpr int kMaxDevices = 64;
 int g_device_ok[kMaxDevices] = {0};  // 0 unknown, 1 gfx950, 2 other
+int g_cu_count[kMaxDevices] = {0};   // 0 unknown
 }  // namespace
 
 namespace moe {
@@ -25,6 +26,17 @@ moe_status_t check_device() {
     __atomic_store_n(&g_device_ok[dev], state, __ATOMIC_RELAXED);
   }
   return state == 1 ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = __atomic_load_n(&g_cu_count[dev], __ATOMIC_RELAXED);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    __atomic_store_n(&g_cu_count[dev], n, __ATOMIC_RELAXED);
+  }
+  return n;
 }
 
 moe_status_t allow_dynamic_lds(const void* func, int bytes, std::atomic<uint64_t>& done) {

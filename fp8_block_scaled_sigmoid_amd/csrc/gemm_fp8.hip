@@ -35,13 +35,13 @@
 //     wave and its up partner swap half of their subtiles through LDS so all
 //     8 waves form h, and the 128 h columns of a row (one 1x128 quantisation
 //     tile) meet in LDS for the tile maximum;
-//   * two K-loop schedules, chosen by the epilogue at compile time (each was
-//     measured faster for its case): with the SwiGLU epilogue (GEMM1) the
-//     "ping-pong" loop, two wave groups alternating MFMA and VALU/memory
-//     phases; with the bf16 and float32 epilogues (GEMM2, Dgrad) the
-//     single-group loop, and a workgroup computes two adjacent column tiles of
-//     the same rows one after the other, the second reusing the group lookup
-//     and the row map;
+//   * two K-loop schedules (each measured faster for its case), chosen per
+//     launch: the "ping-pong" loop, two wave groups alternating MFMA and
+//     VALU/memory phases, for the SwiGLU epilogue (GEMM1) and contractions
+//     longer than 2048; the single-group loop for the short ones (GEMM2),
+//     where a workgroup may compute two adjacent column tiles of the same rows
+//     one after the other, the second reusing the group lookup and the row
+//     map;
 //   * every workgroup derives the tile list itself from the device-side group
 //     offsets (tiles ordered group, column tile (or pair), row tile), so the
 //     call needs no workspace and no host sync; consecutive row tiles of one
@@ -89,6 +89,7 @@ struct GemmParams {
   float* out_d;
   long long ldo;
   const float* row_scale;
+  int cols_per_wg;          // column tiles a workgroup computes one after the other (1 or 2)
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) {
@@ -129,7 +130,7 @@ __device__ __forceinline__ float row_max16(float v) {
   return v;
 }
 
-template <int EPI>
+template <int EPI, bool PING_PONG>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int s_tmp[kThreads];
@@ -139,13 +140,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.G;
   const int n_tiles = (p.n_out + BN - 1) / BN;   // the last tile may be 128 wide
-  // the SwiGLU epilogue runs the ping-pong K loop on one column tile; the
-  // others run the single-group K loop on two adjacent column tiles of the
-  // same rows, one after the other (the second reuses the group lookup and
-  // the row map, so it starts with its copies)
-  constexpr bool kPingPong = EPI == MOE_EPI_SWIGLU_FP8;
-  constexpr int kPer = kPingPong ? 1 : 2;
-  const int n_cols = (n_tiles + kPer - 1) / kPer;
+  // PING_PONG: the ping-pong K loop on one column tile; otherwise the
+  // single-group K loop on one column tile or (cols_per_wg = 2, chosen by
+  // the host) two adjacent ones of the same rows, one after the other (the
+  // second reuses the group lookup and the row map, so it starts with its
+  // copies)
+  constexpr bool kPingPong = PING_PONG;
+  constexpr int kMaxPer = kPingPong ? 1 : 2;
+  const int per = kPingPong ? 1 : (p.cols_per_wg == 2 ? 2 : 1);
+  const int n_cols = (n_tiles + per - 1) / per;
 
   // ---- tile list: tiles are ordered (group, column tile, row tile), and
   // group g owns ceil(rows_g / BM) * n_tiles of them.  Thread t counts the
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   const int m0 = (local - col * mt) * BM;
   const int rows_valid = min(BM, rows_g - m0);
   const int nkb = p.k_dim / BK;
-  const int n_here = min(kPer, n_tiles - kPer * col);   // column tiles of this workgroup
+  const int n_here = min(per, n_tiles - per * col);     // column tiles of this workgroup
 
   // ---- direct-to-LDS sources.  Load j of wave w writes 1 KiB block
   // b = 8 j + w (rows 8 b .. 8 b + 7); lane l fills row 8 b + (l >> 3) at chunk
@@ -240,9 +243,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     sa_off = src * nkb_all * 4;
   }
 #pragma unroll
-  for (int hh = 0; hh < kPer; ++hh) {
+  for (int hh = 0; hh < kMaxPer; ++hh) {
   if (hh >= n_here) break;
-  const int n_tile = kPer * col + hh;
+  const int n_tile = per * col + hh;
   const bool half_tile = p.n_out - n_tile * BN < BN;   // only 128 columns exist
   if (hh > 0) __syncthreads();   // the previous tile's epilogue is done with LDS
 
@@ -736,19 +739,41 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   }
 }
 
+template <int EPI, bool PING_PONG>
+moe_status_t launch_schedule(const GemmParams& q, long long grid, hipStream_t stream) {
+  static std::atomic<uint64_t> lds_set{0};
+  if (moe_status_t st = allow_dynamic_lds(
+          reinterpret_cast<const void*>(&grouped_gemm_kernel<EPI, PING_PONG>), kLds, lds_set))
+    return st;
+  hipLaunchKernelGGL((grouped_gemm_kernel<EPI, PING_PONG>), dim3((unsigned)grid), dim3(kThreads),
+                     kLds, stream, q);
+  return launch_status();
+}
+
+// The schedule by measurement: the ping-pong K loop for the SwiGLU epilogue
+// and for contractions longer than 16 K blocks; the single-group loop for the
+// short ones (K <= 2048, where the per-tile work weighs most), with two column
+// tiles per workgroup as long as the grid still holds at least 32 workgroups
+// per compute unit (so the last, partly filled round stays a small share).
 template <int EPI>
 moe_status_t launch(const GemmParams& p, hipStream_t stream) {
-  static std::atomic<uint64_t> lds_set{0};
-  if (moe_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(&grouped_gemm_kernel<EPI>),
-                                          kLds, lds_set))
-    return st;
-  constexpr long long per = EPI == MOE_EPI_SWIGLU_FP8 ? 1 : 2;   // column tiles per workgroup
-  const long long n_cols = ((p.n_out + BN - 1) / BN + per - 1) / per;
-  long long grid = ((long long)(p.total_rows + BM - 1) / BM + p.G) * n_cols;
+  const bool ping_pong = EPI == MOE_EPI_SWIGLU_FP8 || p.k_dim / BK > 16;
+  const long long n_tiles = (p.n_out + BN - 1) / BN;
+  const long long row_tiles = (long long)(p.total_rows + BM - 1) / BM + p.G;   // an upper bound
+  const long long cus = cu_count();
+  if (cus <= 0) return MOE_ERR_HIP;
+  GemmParams q = p;
+  q.cols_per_wg = (!ping_pong && row_tiles * ((n_tiles + 1) / 2) >= 32 * cus) ? 2 : 1;
+  const long long n_cols = (n_tiles + q.cols_per_wg - 1) / q.cols_per_wg;
+  long long grid = row_tiles * n_cols;
   grid = (grid + 7) / 8 * 8;
   if (grid > 0x7FFFFFFFLL) return MOE_ERR_SHAPE;
-  hipLaunchKernelGGL(grouped_gemm_kernel<EPI>, dim3((unsigned)grid), dim3(kThreads), kLds, stream, p);
-  return launch_status();
+  if constexpr (EPI == MOE_EPI_SWIGLU_FP8) {
+    return launch_schedule<EPI, true>(q, grid, stream);
+  } else {
+    return ping_pong ? launch_schedule<EPI, true>(q, grid, stream)
+                     : launch_schedule<EPI, false>(q, grid, stream);
+  }
 }
 
 }  // namespace

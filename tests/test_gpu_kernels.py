@@ -496,6 +496,42 @@ def test_gemm_many_groups_bit_exact():
     assert np.array_equal(out.cpu().numpy().astype(np.float64), want)
 
 
+@pytest.mark.parametrize("n_out", [6912, 7040])
+def test_gemm_paired_column_tiles_bit_exact(n_out):
+    """A grid large enough (about 75 k rows, 27 or 28 column tiles) that the
+    bf16 and float32 epilogues compute two column tiles per workgroup; an odd
+    count of column tiles (the last pair holds one) and a 128-wide last tile.
+    Integer operands, so every output is exact: sampled rows (every group's
+    first and last rows and ragged tails, and random ones) bit-exact."""
+    moe = _moe()
+    rng = np.random.default_rng(n_out)
+    K = 128
+    sizes = [40000, 17, 35000]
+    off = _ragged_offsets(sizes)
+    R, G = int(off[-1]), len(sizes)
+    aq = _int_codes(rng, (R, K))
+    ad = np.full((R, K // 128), 2.0 ** -3, np.float32)
+    bq = _int_codes(rng, (G, n_out, K))
+    bd = np.full((G, n_out // 128, K // 128), 2.0 ** -5, np.float32)
+    rows = np.unique(np.concatenate([off[:-1], off[1:] - 1, [39999 - 63, 39999 - 64],
+                                     rng.integers(0, R, 200)]))
+    rows_dev = torch.from_numpy(rows.astype(np.int64)).cuda()
+    want = np.zeros((rows.size, n_out))
+    for g in range(G):
+        sel = (rows >= off[g]) & (rows < off[g + 1])
+        if sel.any():
+            want[sel] = ffn.block_scaled_gemm(aq[rows[sel]], ad[rows[sel]], bq[g], bd[g])
+    for epi in (moe.MOE_EPI_F32, moe.MOE_EPI_BF16):
+        log(f"moe_grouped_gemm_fp8 paired columns n_out={n_out} epi={epi}")
+        out, _ = moe.moe_grouped_gemm_fp8(to_dev(aq), to_dev(ad), to_dev(bq), to_dev(bd),
+                                          to_dev(off), R, epi)
+        got = out.index_select(0, rows_dev).float().cpu().numpy().astype(np.float64)
+        del out
+        torch.cuda.synchronize()
+        ref = want if epi == moe.MOE_EPI_F32 else ffn.bf16_round(want)
+        assert np.array_equal(got, ref)
+
+
 def _random_codes(rng, shape):
     c = rng.integers(0, 256, shape).astype(np.uint8)
     return np.where((c & 0x7F) == 0x7F, c & 0xF0, c).astype(np.uint8)   # no NaN codes
