@@ -112,6 +112,39 @@ def test_quant_1x128_f32_encoder_sweep():
     assert np.array_equal(q.cpu().numpy(), e4m3.encode(x.astype(np.float64)))
 
 
+@pytest.mark.slow
+def test_quant_1x128_f32_every_float32_up_to_448():
+    """The hardware E4M3 conversion against the oracle on every float32 of
+    magnitude at most 448 (1.14 G patterns per sign, both signs, -0
+    included): tiles whose maximum is 448 have m = d = 1, so each code is the
+    encoding of that very float.  Negative codes are the positive ones with
+    the sign bit, as the format defines them.  About two minutes."""
+    moe = _moe()
+    top = 0x43E00000 + 1                      # bit patterns 0 .. 448.0
+    step = 1 << 24
+    per = 127
+    bad = 0
+    for n, lo in enumerate(range(0, top, step)):
+        hi = min(lo + step, top)
+        pos = np.arange(lo, hi, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        want_pos = e4m3.encode_arith(pos.astype(np.float64)).astype(np.uint8)
+        vals = np.concatenate([pos, -pos])
+        want = np.concatenate([want_pos, want_pos | np.uint8(0x80)])
+        n_t = (vals.size + per - 1) // per
+        pad = np.full(n_t * per, 448.0, np.float32)
+        pad[:vals.size] = vals
+        tiles = np.concatenate([np.full((n_t, 1), 448.0, np.float32), pad.reshape(n_t, per)], 1)
+        q, d = moe.fp8_quant_1x128(to_dev(tiles))
+        got = q.cpu().numpy()[:, 1:].reshape(-1)[:vals.size]
+        torch.cuda.synchronize()
+        assert np.all(d.cpu().numpy() == 1.0)
+        bad += int(np.count_nonzero(got != want))
+        if n % 8 == 0:
+            print(f"chunk {n}: patterns {lo:#010x}..{hi - 1:#010x}, mismatches so far {bad}",
+                  flush=True)
+    assert bad == 0
+
+
 def test_quant_1x128_f32_random_tiles():
     moe = _moe()
     rng = np.random.default_rng(3)

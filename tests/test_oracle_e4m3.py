@@ -6,6 +6,7 @@ Sources: "DeepSeek-V3 Technical Report" (deepforge.srivtx.xyz), part 1
 exponent) and part 4 "Build it yourself" (the 6-12 % per-element step).
 """
 import math
+import os
 from fractions import Fraction
 
 import numpy as np
@@ -78,6 +79,27 @@ def _ties_and_neighbours():
 def test_two_encoders_agree_on_a_float32_sweep():
     v = _fp32_sweep()
     assert np.array_equal(e4m3.encode_search(v), e4m3.encode_arith(v))
+
+
+def _mismatches_in_chunk(start):
+    """Finite float32 patterns start .. start + 2^24 - 1 on which the two
+    encoders disagree (a worker of the exhaustive test)."""
+    bits = np.arange(start, start + (1 << 24), dtype=np.uint64).astype(np.uint32)
+    v = bits.view(np.float32)
+    v = v[np.isfinite(v)].astype(np.float64)
+    return int(np.count_nonzero(e4m3.encode_search(v) != e4m3.encode_arith(v)))
+
+
+@pytest.mark.slow
+def test_two_encoders_agree_on_every_float32():
+    """Every finite float32 (2^32 - 2^24 patterns, both signs): the table
+    search and the exponent/mantissa encoder give the same code.  About two
+    minutes on 8 cores."""
+    from concurrent.futures import ProcessPoolExecutor
+    starts = [c << 24 for c in range(256)]
+    with ProcessPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        bad = sum(ex.map(_mismatches_in_chunk, starts))
+    assert bad == 0
 
 
 def test_two_encoders_agree_on_ties():
