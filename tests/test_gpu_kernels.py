@@ -599,6 +599,37 @@ def test_gemm_random_operands_f32():
     assert worst <= 1e-4
 
 
+@pytest.mark.parametrize("K", [2048, 7168])
+def test_gemm_single_group_against_library_matmul(K):
+    """A single group holding every row is an ordinary GEMM: compared with
+    torch's float32 matmul (rocBLAS / hipBLASLt, an independent library) on
+    the dequantised operands, within the FP8 MFMA's block-sum band
+    (2^-13 of sum|a*b| per 128-deep block) plus the library's own float32
+    rounding.  K = 2048 runs the single-group K loop, K = 7168 the
+    ping-pong."""
+    moe = _moe()
+    rng = np.random.default_rng(K)
+    M, N = 1000, 512
+    aq = _random_codes(rng, (M, K))
+    ad = rng.uniform(1e-3, 1e-2, (M, K // 128)).astype(np.float32)
+    bq = _random_codes(rng, (1, N, K))
+    bd = rng.uniform(1e-3, 1e-2, (1, N // 128, K // 128)).astype(np.float32)
+    off = np.array([0, M], np.int32)
+    log(f"moe_grouped_gemm_fp8 single group vs torch.matmul K={K}")
+    out, _ = moe.moe_grouped_gemm_fp8(to_dev(aq), to_dev(ad), to_dev(bq), to_dev(bd),
+                                      to_dev(off), M, moe.MOE_EPI_F32)
+    table = torch.from_numpy(e4m3.TABLE.astype(np.float32)).cuda()
+    a = table[to_dev(aq).long()] * to_dev(ad).repeat_interleave(128, dim=1)
+    sb = to_dev(bd[0]).repeat_interleave(128, dim=0).repeat_interleave(128, dim=1)
+    b = table[to_dev(bq[0]).long()] * sb
+    ref = torch.matmul(a, b.t().contiguous())
+    mag = torch.matmul(a.abs(), b.abs().t().contiguous())
+    ratio = ((out - ref).abs() / mag).max().item()
+    torch.cuda.synchronize()
+    print(f"max |ours - library| / sum|a*b| = {ratio:.3e}")
+    assert ratio <= 2e-4
+
+
 def _swiglu_case(integer):
     moe = _moe()
     rng = np.random.default_rng(12)
