@@ -500,6 +500,37 @@ def test_gemm_integer_operands_bit_exact(K, n_out, sizes, gather):
         assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("K", [256, 7168])
+def test_gemm_bf16_row_scale_bit_exact(K):
+    """The bf16 epilogue's per-row multiplier: out = bf16(fl32(C * row_scale))
+    with C exact (integer operands, power-of-two scales), so the result is
+    bit-exact: the float32 product, then round to nearest even bf16.  K = 256
+    runs the single-group K loop, K = 7168 the ping-pong."""
+    moe = _moe()
+    rng = np.random.default_rng(K + 5)
+    sizes = [70, 0, 200, 1]
+    off = _ragged_offsets(sizes)
+    R, G, n_out = int(off[-1]), len(sizes), 384
+    aq = _int_codes(rng, (R + 9, K))
+    ad = np.full((R + 9, K // 128), 2.0 ** -3, np.float32)
+    bq = _int_codes(rng, (G, n_out, K))
+    bd = np.full((G, n_out // 128, K // 128), 2.0 ** -5, np.float32)
+    rix = rng.integers(0, R + 9, R).astype(np.int32)
+    rs = rng.uniform(0.1, 2.0, R).astype(np.float32)
+    c = np.zeros((R, n_out))
+    for g in range(G):
+        rr = np.arange(off[g], off[g + 1])
+        if rr.size:
+            c[rr] = ffn.block_scaled_gemm(aq[rix[rr]], ad[rix[rr]], bq[g], bd[g])
+    want = ffn.bf16_round((c.astype(np.float32) * rs[:, None]).astype(np.float64))
+    log(f"moe_grouped_gemm_fp8 bf16 row_scale K={K}")
+    out, _ = moe.moe_grouped_gemm_fp8(to_dev(aq), to_dev(ad), to_dev(bq), to_dev(bd),
+                                      to_dev(off), R, moe.MOE_EPI_BF16, a_row_index=to_dev(rix),
+                                      row_scale=to_dev(rs))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.float().cpu().numpy().astype(np.float64), want)
+
+
 def test_gemm_many_groups_bit_exact():
     """1025 groups (the most the tile scan takes, three per thread), most of
     them empty, the others of 1 to 140 rows, integer operands: bit-exact."""
