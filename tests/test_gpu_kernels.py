@@ -531,6 +531,46 @@ def test_gemm_bf16_row_scale_bit_exact(K):
     assert np.array_equal(out.float().cpu().numpy().astype(np.float64), want)
 
 
+def test_strided_rows_bit_exact():
+    """Row strides larger than the row: the quantiser reads x as a column
+    slice of a wider bf16 array (ld > cols), and the GEMM reads A as a column
+    slice (lda > K) and writes into a column slice of a wider output
+    (ldo > n_out); all bit-exact against the oracle on the same values."""
+    moe = _moe()
+    rng = np.random.default_rng(77)
+    rows, cols = 300, 512
+    wide = (rng.standard_normal((rows, cols + 384)) * np.exp(rng.uniform(-3, 3, (rows, 1))))
+    wide_b = synth.f32_to_bf16_bits(wide.astype(np.float32))
+    wide_dev = bf16_to_dev(wide_b)
+    log("fp8_quant_1x128 strided rows")
+    q, d = moe.fp8_quant_1x128(wide_dev[:, 128:128 + cols])
+    torch.cuda.synchronize()
+    wq, wd = quant.quant_1x128(synth.as_f64(wide_b[:, 128:128 + cols]))
+    assert np.array_equal(q.cpu().numpy(), wq) and np.array_equal(d.cpu().numpy(), wd)
+
+    K, n_out = 256, 384
+    sizes = [100, 3, 150]
+    off = _ragged_offsets(sizes)
+    R, G = int(off[-1]), len(sizes)
+    a_wide = _int_codes(rng, (R, K + 256))
+    aq = a_wide[:, 128:128 + K]
+    ad = np.full((R, K // 128), 2.0 ** -3, np.float32)
+    bq = _int_codes(rng, (G, n_out, K))
+    bd = np.full((G, n_out // 128, K // 128), 2.0 ** -5, np.float32)
+    want = np.zeros((R, n_out))
+    for g in range(G):
+        rr = np.arange(off[g], off[g + 1])
+        want[rr] = ffn.block_scaled_gemm(aq[rr], ad[rr], bq[g], bd[g])
+    out_wide = torch.zeros(R, n_out + 128, dtype=torch.bfloat16, device="cuda")
+    log("moe_grouped_gemm_fp8 strided A and output")
+    moe.moe_grouped_gemm_fp8(to_dev(a_wide)[:, 128:128 + K], to_dev(ad), to_dev(bq), to_dev(bd),
+                             to_dev(off), R, moe.MOE_EPI_BF16, out=out_wide[:, 64:64 + n_out])
+    torch.cuda.synchronize()
+    got = out_wide.float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(got[:, 64:64 + n_out], ffn.bf16_round(want))
+    assert not got[:, :64].any() and not got[:, 64 + n_out:].any()   # nothing outside the slice
+
+
 def test_gemm_many_groups_bit_exact():
     """1025 groups (the most the tile scan takes, three per thread), most of
     them empty, the others of 1 to 140 rows, integer operands: bit-exact."""
