@@ -428,6 +428,24 @@ def test_gemm2_combine_rounding_faithful(T, H, N, k, I):
     assert err_out <= Q_BAR and err <= Q_BAR
 
 
+def test_layer_empty_batch():
+    """T = 0 through the whole layer: every call is a no-op that succeeds, y
+    is empty, and the bias stays put (zero load equals the zero target)."""
+    moe = _moe()
+    w = synth.WORKLOADS["tiny"]
+    b = w.bias()
+    weights = moe.MoEWeights(bf16_to_dev(w.router_weight()), to_dev(b.copy()),
+                             w1_bf16=bf16_to_dev(synth.generate(w.w1_spec(), w.seed)),
+                             w2_bf16=bf16_to_dev(synth.generate(w.w2_spec(), w.seed)))
+    log("layer T=0")
+    lay = moe.MoELayer(weights, 0, w.k, w.gamma)
+    y = lay.forward(torch.empty(0, w.H, dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (0, w.H)
+    assert np.array_equal(lay.counts.cpu().numpy(), np.zeros(w.N, np.int32))
+    assert np.array_equal(weights.bias.cpu().numpy(), b)
+
+
 @pytest.mark.parametrize("router_fp8", [False, True])
 def test_layer_forward_graph_replay(router_fp8):
     """MoELayer.forward allocates nothing, clears nothing with a memset and
