@@ -428,6 +428,58 @@ def test_gemm2_combine_rounding_faithful(T, H, N, k, I):
     assert err_out <= Q_BAR and err <= Q_BAR
 
 
+def test_layers_on_two_streams_from_two_threads():
+    """The library keeps no state between calls: two layers (own weights and
+    bias), each driven by its own host thread on its own stream (default
+    priority) for three batches, give bit for bit what the same layers give
+    when run one after the other."""
+    import threading
+    moe = _moe()
+    w = synth.Workload("threads", T=300, H=512, N=32, k=4, I=256, x_std=1.0,
+                       wr_dist=synth.NORMAL, wr_param=0.05, bias_half=0.1, w_std=0.02, seed=9)
+    wr = bf16_to_dev(w.router_weight())
+    w1 = bf16_to_dev(synth.generate(w.w1_spec(), w.seed))
+    w2 = bf16_to_dev(synth.generate(w.w2_spec(), w.seed))
+    b0 = to_dev(w.bias().copy())
+    xs = [bf16_to_dev(synth.generate(w.x_spec(b), w.seed)) for b in range(6)]
+
+    def make():
+        weights = moe.MoEWeights(wr, b0.clone(), w1_bf16=w1, w2_bf16=w2)
+        return moe.MoELayer(weights, w.T, w.k, w.gamma)
+
+    # reference: layer A on batches 0-2, then layer B on batches 3-5
+    ref = []
+    for lay, batches in ((make(), xs[:3]), (make(), xs[3:])):
+        ref.append([lay.forward(x).clone() for x in batches] + [lay.w.bias.clone()])
+    torch.cuda.synchronize()
+
+    layers = [make(), make()]
+    results = [None, None]
+    errors = []
+
+    def run(i):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                outs = [layers[i].forward(x, stream=st).clone() for x in xs[3 * i:3 * i + 3]]
+                outs.append(layers[i].w.bias.clone())
+            st.synchronize()
+            results[i] = outs
+        except Exception as e:                     # reported below
+            errors.append(e)
+
+    log("two layers, two streams, two host threads")
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    for i in range(2):
+        for got, want in zip(results[i], ref[i]):
+            assert torch.equal(got, want)
+
+
 def test_layer_empty_batch():
     """T = 0 through the whole layer: every call is a no-op that succeeds, y
     is empty, and the bias stays put (zero load equals the zero target)."""
