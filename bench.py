@@ -18,8 +18,9 @@ region is K steps with an event pair around every launch on the launch stream;
 per-kernel times are the means of those, and each step's time runs from its
 first launch to its last (the median is reported beside the mean).  A second
 pass of K steps, each after a write of --flush-mb MiB that evicts the caches,
-gives the flushed median, and K replays of one step captured in a HIP graph
-the graph step time.  Measured peaks are reported beside the published ones:
+gives the flushed median, K replays of one step captured in a HIP graph the
+graph step time, and K calls of moe_layer_forward (the same kernels behind one
+library call) the native-call step time.  Measured peaks are reported beside the published ones:
 a 2 GiB device copy and the library's FP8 MFMA rate probe.
 --router-fp8 swaps in the opt-in FP8 router (x quantised before routing); the
 routing workload also times the other router on the same batch and reports
@@ -633,6 +634,26 @@ def main():
         del g
     except RuntimeError as err:      # reported, not fatal: the eager numbers stand
         graph_ms = f"capture failed: {err}"
+    # the same step as one library call (moe_layer_forward: the kernels of
+    # step() in the same order, every intermediate in one workspace), K calls
+    ws_native = torch.empty(moe.moe_layer_workspace_bytes(w.T, w.H, w.N, w.k, w.I,
+                                                          lay.with_shared),
+                            dtype=torch.uint8, device=dev)
+
+    def native_step():
+        moe.moe_layer_forward(weights, xs[cur["i"] % len(xs)], w.k, w.gamma,
+                              router_fp8=args.router_fp8, y=lay.y, ws=ws_native, stream=st)
+        cur["i"] += 1
+
+    native_step()
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(args.steps):
+        native_step()
+    e1.record(st)
+    torch.cuda.synchronize()
+    native_ms = e0.elapsed_time(e1) / args.steps
+    del ws_native
     # after the timed region: the per-expert load max/mean of the workload's
     # batches (one more pass over them, each followed by a read of the counts)
     load_ratio = []
@@ -716,6 +737,7 @@ def main():
         "layer_ms_median": round(float(np.median(step_ms)), 4),
         "layer_ms_median_flushed": round(float(np.median(flushed_ms)), 4),
         "graph_ms_per_step": round(graph_ms, 4) if isinstance(graph_ms, float) else graph_ms,
+        "native_call_ms_per_step": round(native_ms, 4),
         "flush_mb": args.flush_mb,
         "measured_peaks": peaks,
         "kernel_ms": {n: round(v, 4) for n, v in kern.items()},

@@ -7,7 +7,8 @@ library is missing or the device is not gfx950 the calls raise.
 
 The functions carry the C entry points' names.  ``MoELayer`` chains them into
 the forward pass (router + biased top-k, permutation, 1x128 activation
-quantisation, the two grouped FP8 GEMMs, combine, bias update).
+quantisation, the two grouped FP8 GEMMs, combine, bias update);
+``moe_layer_forward`` runs the same steps in one library call.
 """
 import ctypes
 import os
@@ -42,6 +43,20 @@ class GemmArgs(ctypes.Structure):
                 ("ldo", ctypes.c_int), ("row_scale", ctypes.c_void_p)]
 
 
+class LayerArgs(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("w_router", ctypes.c_void_p),
+                ("w_router_q", ctypes.c_void_p), ("w_router_d", ctypes.c_void_p),
+                ("bias", ctypes.c_void_p), ("w1_q", ctypes.c_void_p), ("w1_d", ctypes.c_void_p),
+                ("w2_q", ctypes.c_void_p), ("w2_d", ctypes.c_void_p),
+                ("T", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int), ("k", ctypes.c_int),
+                ("I", ctypes.c_int), ("with_shared", ctypes.c_int), ("n_groups", ctypes.c_int),
+                ("topk_groups", ctypes.c_int), ("router_fp8", ctypes.c_int),
+                ("update_bias", ctypes.c_int), ("gamma", ctypes.c_float),
+                ("residual", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("scores", ctypes.c_void_p), ("topk_idx", ctypes.c_void_p),
+                ("topk_gate", ctypes.c_void_p), ("counts", ctypes.c_void_p)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -71,6 +86,7 @@ def lib():
             "fp8_quant_tokens_128": [_P, _I, _I, _I, _LL, _P, _I, _P, _P, _LL, _P, _P],
             "moe_grouped_wgrad_fp8": [_P, _P, _LL, _I, _P, _P, _LL, _I, _P, _I, _P, _P],
             "moe_probe_fp8_mfma": [_I, _I, _P, _P],
+            "moe_layer_forward": [ctypes.POINTER(LayerArgs), _P, ctypes.c_size_t, _P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -80,6 +96,8 @@ def lib():
         L.moe_permute_workspace_bytes.restype = ctypes.c_size_t
         L.moe_route_workspace_bytes.argtypes = [_I, _I, _I]
         L.moe_route_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_layer_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
+        L.moe_layer_workspace_bytes.restype = ctypes.c_size_t
         L.moe_status_str.argtypes = [_I]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_last_hip_error.argtypes = []
@@ -376,6 +394,39 @@ def moe_probe_fp8_mfma(blocks, iters, sink=None, stream=None):
     _check("moe_probe_fp8_mfma", lib().moe_probe_fp8_mfma(blocks, iters, _ptr(sink),
                                                           _stream(stream)))
     return sink, float(blocks) * 4 * iters * 16 * 65536
+
+
+def moe_layer_workspace_bytes(T, H, N, k, I, with_shared=True):
+    return int(lib().moe_layer_workspace_bytes(T, H, N, k, I, 1 if with_shared else 0))
+
+
+def moe_layer_forward(w, x, k, gamma=1e-3, n_groups=1, topk_groups=1, router_fp8=False,
+                      update_bias=True, residual=None, y=None, scores=None, idx=None, gate=None,
+                      counts=None, ws=None, stream=None):
+    """The whole forward pass in one library call (moe_layer_forward): w a
+    MoEWeights, x [T,H] bf16.  Returns y [T,H] bf16.  scores / idx / gate /
+    counts: optional device outputs.  ws: optional uint8 device workspace of
+    moe_layer_workspace_bytes(...) bytes (allocated here when None)."""
+    T, H = x.shape
+    _dev(x, torch.bfloat16, "x"), _dev(w.bias, torch.float32, "bias")
+    with_shared = w.G == w.N + 1
+    if router_fp8 and w.w_router_q is None:
+        raise ValueError("router_fp8 needs MoEWeights(..., router_fp8=True)")
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=x.device) if y is None else y
+    if ws is None:
+        ws = torch.empty(max(moe_layer_workspace_bytes(T, H, w.N, k, w.I, with_shared), 256),
+                         dtype=torch.uint8, device=x.device)
+    a = LayerArgs(x.data_ptr(), w.w_router.data_ptr(),
+                  w.w_router_q.data_ptr() if w.w_router_q is not None else None,
+                  w.w_router_d.data_ptr() if w.w_router_d is not None else None,
+                  w.bias.data_ptr(), w.w1q.data_ptr(), w.w1d.data_ptr(), w.w2q.data_ptr(),
+                  w.w2d.data_ptr(), T, H, w.N, k, w.I, 1 if with_shared else 0, n_groups,
+                  topk_groups, 1 if router_fp8 else 0, 1 if update_bias else 0, float(gamma),
+                  residual.data_ptr() if residual is not None else None, y.data_ptr(),
+                  *[t.data_ptr() if t is not None else None for t in (scores, idx, gate, counts)])
+    _check("moe_layer_forward", lib().moe_layer_forward(ctypes.byref(a), _ptr(ws), ws.numel(),
+                                                        _stream(stream)))
+    return y
 
 
 # ---------------------------------------------------------------------------

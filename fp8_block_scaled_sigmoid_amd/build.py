@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "libmoe_fp8.so")
 SYNTH_LIB = os.path.join(ROOT, "synth", "libsynth.so")
 
 SOURCES = ["common.hip", "quant.hip", "route.hip", "permute.hip", "gemm_fp8.hip", "combine.hip",
-           "backward.hip", "probe.hip"]
+           "backward.hip", "probe.hip", "layer.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

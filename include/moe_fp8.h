@@ -330,6 +330,69 @@ moe_status_t moe_grouped_wgrad_fp8(const uint8_t* a_q, const float* a_d, long lo
  */
 moe_status_t moe_probe_fp8_mfma(int blocks, int iters, float* sink, hipStream_t stream);
 
+/*
+ * The whole forward pass of one layer in one call ([TP] section III flowchart
+ * and Figure 2; [VE] recipe steps 4-7), enqueued on `stream` in this order:
+ *   FP8 router only: fp8_quant_1x128(x) ahead of the routing;
+ *   moe_route_topk (or moe_route_topk_fp8 when router_fp8) -> idx, gate;
+ *   moe_permute (counts, offsets, row_of, token_of; with_shared appends the
+ *     shared expert as group N);
+ *   bf16 router: fp8_quant_1x128(x);
+ *   moe_grouped_gemm_fp8 with MOE_EPI_SWIGLU_FP8 over the G = N (+1) groups,
+ *     A = the quantised x gathered through token_of, B = W1 -> h codes/scales;
+ *   moe_grouped_gemm_fp8 with MOE_EPI_BF16, A = h, B = W2 -> expert rows;
+ *   moe_combine (shared row T*k + t when with_shared) -> y;
+ *   moe_bias_update(bias, counts) when update_bias.
+ * Each step computes exactly what its own entry point computes, so the
+ * results are bit-identical to calling the steps one by one.
+ * Operands (device pointers; shapes with R = T*k + (with_shared ? T : 0)):
+ *   x bf16 [T,H]; w_router bf16 [N,H] (bf16 router) or w_router_q E4M3 [N,H]
+ *   with w_router_d float [N/128,H/128] (router_fp8); bias float [N], updated
+ *   in place when update_bias; w1_q E4M3 [G,2I,H] gate/up interleaved with
+ *   w1_d float [G,2I/128,H/128] (fp8_quant_128x128 with interleave_gate_up);
+ *   w2_q E4M3 [G,H,I] with w2_d float [G,H/128,I/128]; residual bf16 [T,H]
+ *   or NULL; y bf16 [T,H] (written).  Optional outputs, each NULL to skip:
+ *   scores float [T,N], topk_idx int32 [T,k], topk_gate float [T,k],
+ *   counts int32 [N] (when NULL these live in the workspace).
+ * ws: device scratch of at least moe_layer_workspace_bytes(T, H, N, k, I,
+ * with_shared) bytes, 256-byte aligned (MOE_ERR_WORKSPACE / MOE_ERR_ALIGN);
+ * it holds every intermediate (about R * (H * 2 + I + I / 32) + T * H bytes),
+ * so the call allocates nothing and may be captured in a HIP graph.  Calls
+ * that share a workspace must be ordered on one stream.
+ * Requires H % 128 == 0, I % 128 == 0, H, I <= 16384, 16 <= N <= 256,
+ * N % 16 == 0 (N % 128 == 0 and N >= 128 with router_fp8), 1 <= k <= min(N, 32),
+ * the group conditions of moe_route_topk (MOE_ERR_SHAPE); T * H * 2, R * H
+ * and R * I below 2^31 (MOE_ERR_UNSUPPORTED).  Every check runs before the
+ * first launch.
+ */
+typedef struct {
+  const void* x;
+  const void* w_router;
+  const uint8_t* w_router_q;
+  const float* w_router_d;
+  float* bias;
+  const uint8_t* w1_q;
+  const float* w1_d;
+  const uint8_t* w2_q;
+  const float* w2_d;
+  int T, H, N, k, I;
+  int with_shared;              /* nonzero: expert N is the shared expert */
+  int n_groups, topk_groups;    /* group-limited selection when n_groups > 1 */
+  int router_fp8;               /* nonzero: the opt-in FP8 router */
+  int update_bias;              /* nonzero: sign update of bias after combine */
+  float gamma;                  /* bias update speed */
+  const void* residual;
+  void* y;
+  float* scores;
+  int32_t* topk_idx;
+  float* topk_gate;
+  int32_t* counts;
+} moe_layer_args;
+
+size_t moe_layer_workspace_bytes(int T, int H, int N, int k, int I, int with_shared);
+moe_status_t moe_layer_forward(const moe_layer_args* args, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char* moe_status_str(moe_status_t status);
 /* hipError_t of the most recent MOE_ERR_HIP on this thread (0 if none). */

@@ -162,3 +162,62 @@ def test_gemm_validation(lib):
     assert lib.moe_grouped_gemm_fp8(ctypes.byref(a), None) == 0   # nothing to do
     a.total_rows, a.epilogue, a.out_d = 8, 1, None
     assert lib.moe_grouped_gemm_fp8(ctypes.byref(a), None) == 1   # SwiGLU needs out_d
+
+
+def _layer_args(**kw):
+    from fp8_block_scaled_sigmoid_amd import LayerArgs
+    a = dict(x=16, w_router=16, w_router_q=None, w_router_d=None, bias=16, w1_q=16, w1_d=16,
+             w2_q=16, w2_d=16, T=8, H=256, N=16, k=2, I=128, with_shared=1, n_groups=1,
+             topk_groups=1, router_fp8=0, update_bias=1, gamma=1e-3, residual=None, y=16,
+             scores=None, topk_idx=None, topk_gate=None, counts=None)
+    a.update(kw)
+    return LayerArgs(**a)
+
+
+def test_layer_workspace_bytes(lib):
+    lib.moe_layer_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_layer_workspace_bytes.argtypes = [ctypes.c_int] * 6
+    T, H, N, k, I = 300, 512, 32, 4, 256
+    R = T * k + T
+    got = lib.moe_layer_workspace_bytes(T, H, N, k, I, 1)
+    parts = (3 * T * k * 4 + N * 4 + (N + 2) * 4 + R * 4 + T * H + T * (H // 128) * 4 + R * I
+             + R * (I // 128) * 4 + R * H * 2)
+    assert parts <= got <= parts + 15 * 256 + 4 * T * N * 64
+    assert got % 256 == 0
+    assert lib.moe_layer_workspace_bytes(T, H, N, k, I, 0) < got          # no shared rows
+    assert lib.moe_layer_workspace_bytes(T, 500, N, k, I, 1) == 0         # H % 128
+    assert lib.moe_layer_workspace_bytes(T, H, N, k, 100, 1) == 0         # I % 128
+    assert lib.moe_layer_workspace_bytes(0, H, N, k, I, 1) > 0            # counts, offsets
+
+
+def test_layer_validation_before_any_launch(lib):
+    P = ctypes.c_void_p
+    from fp8_block_scaled_sigmoid_amd import LayerArgs
+    lib.moe_layer_forward.argtypes = [ctypes.POINTER(LayerArgs), P, ctypes.c_size_t, P]
+    lib.moe_layer_forward.restype = ctypes.c_int
+    lib.moe_layer_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_layer_workspace_bytes.argtypes = [ctypes.c_int] * 6
+    need = lib.moe_layer_workspace_bytes(8, 256, 16, 2, 128, 1)
+    ws = P(4096)
+
+    def call(a, ws=ws, n=need):
+        return lib.moe_layer_forward(ctypes.byref(a), ws, n, None)
+
+    assert lib.moe_layer_forward(None, ws, need, None) == 1             # MOE_ERR_NULL
+    assert call(_layer_args(H=200)) == 2                                  # MOE_ERR_SHAPE
+    assert call(_layer_args(I=100)) == 2
+    assert call(_layer_args(N=8)) == 2
+    assert call(_layer_args(k=17)) == 2                                   # k > N
+    assert call(_layer_args(router_fp8=1, w_router_q=16, w_router_d=16)) == 2   # N < 128
+    assert call(_layer_args(n_groups=3)) == 2                             # N % groups
+    assert call(_layer_args(n_groups=4, topk_groups=2, k=3)) == 2         # k % topk_groups
+    assert call(_layer_args(T=1 << 20, H=2048)) == 6                      # MOE_ERR_UNSUPPORTED
+    assert call(_layer_args(bias=None)) == 1
+    assert call(_layer_args(w_router=None)) == 1
+    assert call(_layer_args(router_fp8=1, N=128)) == 1                    # no FP8 router weight
+    assert call(_layer_args(y=None)) == 1
+    assert call(_layer_args(), ws=None) == 4                              # MOE_ERR_WORKSPACE
+    assert call(_layer_args(), n=need - 1) == 4
+    assert call(_layer_args(), ws=P(4096 + 16)) == 3                      # MOE_ERR_ALIGN
+    assert call(_layer_args(x=24)) == 3
+    assert call(_layer_args(w1_q=8)) == 3
