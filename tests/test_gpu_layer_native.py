@@ -181,3 +181,38 @@ def test_native_layer_graph_replay():
         torch.cuda.synchronize()
         assert torch.equal(y_static, y_e), f"replay {b}: output differs"
         assert torch.equal(nat_w.bias, ref_w.bias), f"replay {b}: bias differs"
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_native_layer_v3_shape_matches_step_by_step(name):
+    """At the DeepSeek-V3 shapes (H 7168, 256 routed experts top-8 + 1 shared,
+    I 2048; T = 512 and 8192), one moe_layer_forward call gives bit for bit
+    the step-by-step path's output, routing, counts and updated bias (which the
+    layer tests hold against the oracle on sampled experts)."""
+    from helpers import device_tensor
+    moe = _moe()
+    w = synth.WORKLOADS[name]
+    log(f"moe_layer_forward v3 {name} T={w.T}")
+    w1 = device_tensor(w.w1_spec(), w.seed)
+    w1q, w1d = moe.fp8_quant_128x128(w1, interleave_gate_up=True)
+    del w1
+    w2 = device_tensor(w.w2_spec(), w.seed)
+    w2q, w2d = moe.fp8_quant_128x128(w2)
+    del w2
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    wr = bf16_to_dev(w.router_weight())
+    b0 = to_dev(w.bias().copy())
+    ref_w = moe.MoEWeights(wr, b0.clone(), w1q=w1q, w1d=w1d, w2q=w2q, w2d=w2d)
+    nat_w = moe.MoEWeights(wr, b0.clone(), w1q=w1q, w1d=w1d, w2q=w2q, w2d=w2d)
+    x = device_tensor(w.x_spec(), w.seed)
+    lay = moe.MoELayer(ref_w, w.T, w.k, w.gamma)
+    y_ref = lay.forward(x)
+    out = _outputs(w.T, w.N, w.k)
+    y = moe.moe_layer_forward(nat_w, x, w.k, w.gamma, **out)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    assert torch.equal(out["idx"], lay.idx)
+    assert torch.equal(out["counts"], lay.counts)
+    assert torch.equal(nat_w.bias, ref_w.bias)
+    assert not torch.equal(nat_w.bias, b0)
