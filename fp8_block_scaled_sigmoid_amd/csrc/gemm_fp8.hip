@@ -120,14 +120,30 @@ __device__ __forceinline__ void wait_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Maximum over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15): swap
-// neighbours, swap pairs, mirror the 8-lane halves, mirror the row.
-__device__ __forceinline__ float row_max16(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
-  return v;
+// Row maxima of 16 values per lane (a[r], r = 0..15) over the 16 lanes of
+// each row group, by recursive halving: at each of four exchanges (partner
+// lane = lane ^ 15, ^ 7, ^ 2, ^ 1 within the 16) a lane keeps the half of its
+// values picked by one bit of its lane index and sends the other half, so the
+// lane with row-group index r ends with the maximum of value r over all 16
+// lanes (60 instructions instead of 16 separate reductions).  The values are
+// bit patterns of non-negative floats, whose order is the unsigned order.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t row_max16_halving(const uint32_t (&a)[16], int lrow) {
+  uint32_t b[8], c[4], d[2];
+  const bool s3 = lrow & 8, s2 = lrow & 4, s1 = lrow & 2, s0 = lrow & 1;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    b[i] = max(s3 ? a[i + 8] : a[i], dpp<0x140>(s3 ? a[i] : a[i + 8]));    // row mirror: ^15
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    c[i] = max(s2 ? b[i + 4] : b[i], dpp<0x141>(s2 ? b[i] : b[i + 4]));    // half mirror: ^7
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    d[i] = max(s1 ? c[i + 2] : c[i], dpp<0x4E>(s1 ? c[i] : c[i + 2]));     // quad perm: ^2
+  return max(s0 ? d[1] : d[0], dpp<0xB1>(s0 ? d[0] : d[1]));               // quad perm: ^1
 }
 
 template <int EPI, bool PING_PONG>
@@ -643,26 +659,36 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
           ex[(wave * 32 + (mi * 2 + j) * 4 + v) * 64 + lane] =
               gate_wave ? acc[mi][2 + j][v] : acc[mi][j][v];   // static indices: acc stays in registers
     __syncthreads();
+    // 16-row subtiles past the group's end (wave-uniform) form no h
     float h[4][2][4];
+    uint32_t mxb[16];   // per (mi, v): bits of max |h| over this lane's two columns
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi) {
+      const bool live = wm * 64 + mi * 16 < rows_valid;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int row = wm * 64 + mi * 16 + 4 * lk + v;
         float mx = 0.0f;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const float mine = gate_wave ? acc[mi][j][v] : acc[mi][2 + j][v];
-          const float other = ex[(partner * 32 + (mi * 2 + j) * 4 + v) * 64 + lane];
-          const float gt = gate_wave ? mine : other;
-          const float u = gate_wave ? other : mine;
-          const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gt));
-          h[mi][j][v] = gt * sg * u;
-          mx = fmaxf(mx, fabsf(h[mi][j][v]));
+          h[mi][j][v] = 0.0f;
+          if (live) {
+            const float mine = gate_wave ? acc[mi][j][v] : acc[mi][2 + j][v];
+            const float other = ex[(partner * 32 + (mi * 2 + j) * 4 + v) * 64 + lane];
+            const float gt = gate_wave ? mine : other;
+            const float u = gate_wave ? other : mine;
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gt));
+            h[mi][j][v] = gt * sg * u;
+            mx = fmaxf(mx, fabsf(h[mi][j][v]));
+          }
         }
-        mx = row_max16(mx);
-        if (lrow == 0) red[wn * 128 + row] = mx;
+        mxb[mi * 4 + v] = __float_as_uint(mx);
       }
+    }
+    {
+      // lane (lk, lrow) ends with the maximum of row (mi, v) = (lrow / 4, lrow % 4)
+      const uint32_t mx = row_max16_halving(mxb, lrow);
+      red[wn * 128 + wm * 64 + (lrow >> 2) * 16 + 4 * lk + (lrow & 3)] = __uint_as_float(mx);
+    }
     __syncthreads();
     // one thread per row forms the tile's scale (two divisions) and stores d
     const int ld_d = p.n_out / BN;  // h scale row stride (h has n_out/2 columns)
@@ -676,7 +702,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     __syncthreads();
     const int hc = (wn & 1) * 64;   // this wave's 64-column half of the h tile
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi) {
+      if (wm * 64 + mi * 16 >= rows_valid) continue;   // rows that are not stored
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = wm * 64 + mi * 16 + 4 * lk + v;
@@ -685,6 +712,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
         for (int j = 0; j < 2; ++j)
           otile[row * 128 + hc + (keep0 + j) * 16 + lrow] = (uint8_t)quant_code(h[mi][j][v], m);
       }
+    }
     __syncthreads();
     uint8_t* out = static_cast<uint8_t*>(p.out);
 #pragma unroll
@@ -698,7 +726,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   } else if (EPI == MOE_EPI_BF16) {
     uint16_t* otile = reinterpret_cast<uint16_t*>(smem);   // [128][256] bf16
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi) {
+      if (wm * 64 + mi * 16 >= rows_valid) continue;   // rows that are not stored
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = wm * 64 + mi * 16 + 4 * lk + v;
@@ -710,6 +739,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
           otile[row * 256 + wn * 64 + ni * 16 + lrow] = (uint16_t)f32_to_bf16(val);
         }
       }
+    }
     __syncthreads();
     uint16_t* out = static_cast<uint16_t*>(p.out);
 #pragma unroll
