@@ -85,22 +85,96 @@ def codes_agree_up_to_ties(got, want, scaled_oracle, rel=2e-5):
     return int(diff.sum())
 
 
-def check_h(hq, hd, h, max_frac=5e-2):
-    """The re-quantised intermediate h of the FP8 GEMM path against the
-    oracle's h (float64 [rows, I]).  The GPU's h carries the MFMA block-sum
-    error (~1e-5 of sum|a*b|), so instead of exact codes: the scales within
-    5e-4, every dequantised value within half an E4M3 step of h plus 1e-3 of
-    its tile maximum, and at most `max_frac` of the codes different.  Returns
-    the number of differing codes."""
-    from oracle import quant
+# The FP8 MFMA block-sum bound (per output): gfx950's v_mfma_f32_16x16x128_f8f6f4
+# sums each group of 8 products on a grid 2^-13 below the group's largest
+# (test_mfma_block_sum_precision_probe), so one 128-deep block loses at most
+# about 2^-13 of its absolute sum; accumulated over K blocks, and measured
+# against an independent float32 library matmul at 1.9e-5 and 3.7e-5 of
+# sum |a b|, the bar used throughout is
+MFMA_REL = 1e-4          # |error| <= MFMA_REL * sum_kb |block product| d_A d_B
+# Measured share of h codes that land on the neighbouring E4M3 value of the
+# oracle's (each a value within the MFMA band of a rounding midpoint): 0.1-0.2 %
+# at the prefill and decode shapes.  The bar allows 3x the upper figure.
+H_FLIP_MAX_FRAC = 6e-3
+
+
+def abs_codes(q):
+    """E4M3 codes of |value| (the sign bit cleared)."""
+    return np.asarray(q, np.uint8) & np.uint8(0x7F)
+
+
+def swiglu_band(xq, xd, w1q, w1d, h_ref, a_ref):
+    """Per-element bound on |h_gpu - h_oracle| from the MFMA block-sum bound,
+    propagated through h = SiLU(g) * u:  |dh| <= |u| |SiLU'(g)| |dg| +
+    |SiLU(g)| |du|, with |dg|, |du| <= MFMA_REL * (the same block-scaled GEMM on
+    |codes|), plus a few float32 ulps of the SwiGLU arithmetic itself."""
+    from oracle import ffn
+    mag = ffn.block_scaled_gemm(abs_codes(xq), xd, abs_codes(w1q), w1d)
+    I = h_ref.shape[1]
+    g, u = a_ref[:, :I], a_ref[:, I:]
+    sg = 1.0 / (1.0 + np.exp(-g))
+    dsilu = np.abs(sg * (1.0 + g * (1.0 - sg)))         # |d SiLU / dg| <= 1.1
+    band = MFMA_REL * (np.abs(u) * dsilu * mag[:, :I] + np.abs(g * sg) * mag[:, I:])
+    return band + 8 * 2.0 ** -24 * np.abs(h_ref)
+
+
+def flip_cap(n_codes, max_frac=H_FLIP_MAX_FRAC):
+    """Largest allowed count of differing h codes among n_codes: the 1e-9
+    upper quantile of a Poisson count whose mean is max_frac * n_codes (3x
+    the measured flip rate), so a small sample is not failed by one or two
+    legitimate flips while a large one is held to about max_frac."""
+    from scipy.stats import poisson
+    return int(poisson.ppf(1.0 - 1e-9, max_frac * n_codes))
+
+
+def check_h(hq, hd, res_q, band, max_frac=H_FLIP_MAX_FRAC, max_flips=None):
+    """The GPU's re-quantised intermediate h against the oracle's "Q" expert
+    result ``res_q`` (dict with h, hq, hd) given the per-element bound
+    ``band`` on |h_gpu - h_oracle| (swiglu_band):
+      * each tile's scale within the band of the tile's largest |h|;
+      * every dequantised GPU value within half an E4M3 step of the oracle's
+        h plus the band (scaled);
+      * a code differs from the oracle's only where the oracle's scaled value
+        lies within the band of a rounding midpoint, and then it is the
+        rounding of a value inside the band;
+      * at most flip_cap(codes, max_frac) codes differ (or ``max_flips``).
+    Returns the number of differing codes."""
+    from oracle import e4m3, quant
+    h = res_q["h"]
     rows, I = h.shape
-    wq, wd = quant.quant_1x128(h)
-    np.testing.assert_allclose(hd, wd, rtol=5e-4)
+    hd_ref = np.asarray(res_q["hd"], np.float64)
+    hd = np.asarray(hd, np.float64)
     amax = np.abs(h).reshape(rows, I // 128, 128).max(-1)
+    band_t = band.reshape(rows, I // 128, 128).max(-1)
+    # d = amax / 448 correctly rounded on both sides, amax moved by <= band
+    assert np.all(np.abs(hd - hd_ref) <= (band_t / 448.0) * (1 + 2.0 ** -22) + 2.0 ** -23 * hd_ref), \
+        "h scale outside the MFMA band"
+    m_ref = np.repeat(np.where(amax > 0, 448.0 / np.maximum(amax, 1e-300), 0.0), 128, 1)
+    dd = np.repeat(hd, 128, 1)
     hh = quant.dequant_1x128(hq, hd)
-    dd = np.repeat(np.asarray(hd, np.float64), 128, 1)
-    band = 2.0 ** -4 * np.abs(h) + 2.0 ** -10 * dd + 1e-3 * np.repeat(amax, 128, 1)
-    assert np.all(np.abs(hh - h) <= band), "dequantised h outside the E4M3 + MFMA band"
-    n = int(np.sum(np.asarray(hq) != wq))
-    assert n <= max_frac * wq.size, f"{n} of {wq.size} h codes differ"
+    rel_d = np.repeat(np.abs(hd - hd_ref) / np.maximum(hd_ref, 1e-300), 128, 1)
+    half_step = 2.0 ** -4 * np.abs(h) + 2.0 ** -10 * dd
+    assert np.all(np.abs(hh - h) <= half_step + band * (1 + 2.0 ** -3) + rel_d * np.abs(h)), \
+        "dequantised h outside half an E4M3 step plus the MFMA band"
+    diff = np.asarray(hq) != np.asarray(res_q["hq"])
+    n = int(diff.sum())
+    if n:
+        scaled = np.abs(h[diff]) * m_ref[diff]
+        tol = (band[diff] + rel_d[diff] * np.abs(h[diff])) * m_ref[diff] * (1 + 2.0 ** -10)
+        pos = e4m3.POS_VALUES
+        mids = (pos[:-1] + pos[1:]) / 2
+        i = np.clip(np.searchsorted(mids, scaled), 1, mids.size - 1)
+        dist = np.minimum(np.abs(scaled - mids[i - 1]), np.abs(scaled - mids[i]))
+        assert np.all(dist <= tol + 2.0 ** -20), "an h code differs away from a rounding midpoint"
+        # the GPU code is the rounding of some value within tol of the
+        # oracle's scaled value: rounding is monotone, so it lies between the
+        # roundings of the interval's ends (one step either way, or, for |h|
+        # below the band, the subnormals on either side of zero)
+        s = h[diff] * m_ref[diff]
+        vg = e4m3.decode(np.asarray(hq)[diff])
+        lo = e4m3.round_to_e4m3(s - tol)
+        hi = e4m3.round_to_e4m3(s + tol)
+        assert np.all((lo <= vg) & (vg <= hi)), "an h code is not a rounding of a value inside the band"
+    cap = flip_cap(h.size, max_frac) if max_flips is None else max_flips
+    assert n <= cap, f"{n} of {h.size} h codes differ (cap {cap}, rate bar {max_frac:.1e})"
     return n
