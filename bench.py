@@ -81,9 +81,10 @@ def measured_traffic(workload):
 
 def measured_peaks(moe, torch, st):
     """What the device reaches in practice, beside the published peaks: a
-    plain 2 GiB device-to-device copy (read + write bytes per second) and the
-    FP8 MFMA rate probe of the library (back-to-back 16x16x128 FP8 MFMAs, four
-    waves per SIMD, no memory traffic)."""
+    plain 2 GiB device-to-device copy (read + write bytes per second), the
+    library's HBM probe reading 2 GiB and writing 2 GiB (16-byte accesses;
+    the faster of two read modes and of two write modes), and the FP8 MFMA rate probe (back-to-back
+    16x16x128 FP8 MFMAs, four waves per SIMD, no memory traffic)."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n = 1 << 31
     src = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -96,6 +97,16 @@ def measured_peaks(moe, torch, st):
     e1.record(st)
     torch.cuda.synchronize()
     copy_ms = e0.elapsed_time(e1) / 5
+    stream_ms = {}
+    for mode, name in ((0, "read_nt8"), (1, "write_nt"), (2, "read_plain4"), (3, "write_plain")):
+        moe.moe_probe_hbm(mode, src, stream=st)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(5):
+            moe.moe_probe_hbm(mode, src, stream=st)
+        e1.record(st)
+        torch.cuda.synchronize()
+        stream_ms[name] = e0.elapsed_time(e1) / 5
     del src, dst
     blocks, iters = 256 * 4, 4000
     sink, _ = moe.moe_probe_fp8_mfma(blocks, 8)
@@ -107,8 +118,30 @@ def measured_peaks(moe, torch, st):
     mfma_ms = e0.elapsed_time(e1)
     return {"copy_bytes_read": n, "copy_bytes_written": n, "copy_ms": round(copy_ms, 4),
             "copy_GBps_read_plus_write": round(2 * n / (copy_ms * 1e-3) / 1e9, 1),
+            "read_GBps": round(n / (min(stream_ms["read_nt8"], stream_ms["read_plain4"]) * 1e-3) / 1e9, 1),
+            "write_GBps": round(n / (min(stream_ms["write_nt"], stream_ms["write_plain"]) * 1e-3) / 1e9, 1),
+            "probe_GBps": {k: round(n / (v * 1e-3) / 1e9, 1) for k, v in stream_ms.items()},
             "fp8_mfma_probe_ms": round(mfma_ms, 4),
             "fp8_mfma_TFLOPs": round(flops / (mfma_ms * 1e-3) / 1e12, 1)}
+
+
+def attainable_GBps(read_bytes, write_bytes, peaks):
+    """The measured rate for a step's own mix of reads and writes: its reads
+    at the measured read-only rate and its writes at the measured write-only
+    rate, one after the other ((r + w) / (r / R + w / W)); a plain copy, which
+    overlaps the two, is reported beside it."""
+    t = read_bytes / peaks["read_GBps"] + write_bytes / peaks["write_GBps"]
+    return (read_bytes + write_bytes) / t if t > 0 else 0.0
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def parse():
@@ -126,6 +159,8 @@ def parse():
                     help="also report the 2 GiB device copy under its own key (the reference "
                          "for the HBM byte counters; the copy itself always runs, as one of "
                          "the measured peaks)")
+    ap.add_argument("--no-sub-workloads", action="store_true",
+                    help="skip the decode and skew sub-results of the default prefill run")
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="size of the write that precedes every step of the flushed pass")
     return ap.parse_args()
@@ -181,6 +216,7 @@ def cpu_baseline(w, sample_tokens=None):
     t_tail = time.perf_counter() - t2
     t_total = t_route + t_tail + t_ffn / rows_done * (S * (w.k + 1))
     return {"value": S / t_total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": (f"{S} tokens of the {w.name} batch: routing, quantisation, permutation, "
                        f"combine and bias update on all {S}; expert FFN timed on {rows_done} rows "
                        f"(shared expert + 2 most-loaded routed experts) and scaled per row to "
@@ -207,20 +243,25 @@ def cpu_baseline_routing(w):
     obias.bias_update(b, counts, w.T, w.k, w.gamma)
     dt = time.perf_counter() - t0
     return {"value": w.T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"all {w.T} tokens of the {w.name} batch (router, top-k, gates, counts, "
                       f"permutation, bias update)", "measured_s": round(dt, 3)}
 
 
-def route_bytes_of(T, H, N, k, fp8):
-    """Algorithmic HBM bytes of the routing step: x and Wr read once (bf16, or
-    for the FP8 router x bf16 read by the quantiser, its codes and scales
-    written and read back, Wr codes and scales read), bias read, scores and
-    (index, gate) pairs written."""
-    out = N * 4 + T * N * 4 + T * k * 8
+def route_rw_of(T, H, N, k, fp8):
+    """Algorithmic HBM bytes (read, written) of the routing step: x and Wr
+    read once (bf16, or for the FP8 router x bf16 read by the quantiser, its
+    codes and scales written and read back, Wr codes and scales read), bias
+    read, scores and (index, gate) pairs written."""
+    wr = T * N * 4 + T * k * 8
     if not fp8:
-        return out + T * H * 2 + N * H * 2
+        return T * H * 2 + N * H * 2 + N * 4, wr
     xq = T * H + T * (H // 128) * 4
-    return out + T * H * 2 + 2 * xq + N * H + (N // 128) * (H // 128) * 4
+    return T * H * 2 + xq + N * H + (N // 128) * (H // 128) * 4 + N * 4, wr + xq
+
+
+def route_bytes_of(T, H, N, k, fp8):
+    return sum(route_rw_of(T, H, N, k, fp8))
 
 
 def bench_routing(args, w, moe, torch, gen, wr, bias, st):
@@ -320,6 +361,8 @@ def bench_routing(args, w, moe, torch, gen, wr, bias, st):
         "kernel_ms": {n: round(v, 4) for n, v in kern.items()},
         "step_ms_median": round(float(np.median(step_ms)), 4),
         "route_frac_measured_copy_peak": round(gbs / copy_gbs, 4),
+        "route_frac_measured_read_write_mix": round(
+            gbs / attainable_GBps(*route_rw_of(T, H, N, k, args.router_fp8), peaks), 4),
         "measured_peaks": peaks,
         "other_router": {"router": "bf16" if args.router_fp8 else "fp8",
                          "route_ms": round(other_ms, 4),
@@ -503,9 +546,147 @@ def cpu_baseline_backward(w, R):
     backward.wgrad(d_a, x, off)
     dt = time.perf_counter() - t0
     return {"value": w.T / (dt / S * R), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{S} expert rows in 16 groups of 256: Dgrad and Wgrad of both expert "
                       f"GEMMs with their quantisers, scaled per row to {R} rows",
             "measured_s": round(dt, 3)}
+
+
+def layer_step_fns(lay, xs, cur, router_fp8):
+    """The launches of one layer step, in order, with their names."""
+    names = ["route", "permute", "quant_x", "gemm1", "gemm2", "combine", "bias"]
+    fns = [lambda: lay.route(xs[cur["i"] % len(xs)]), lay.permute,
+           lambda: lay.quant_x(xs[cur["i"] % len(xs)]), lay.gemm1, lay.gemm2,
+           lay.combine, lay.bias_update]
+    if router_fp8:    # the FP8 router reads the quantised x: quantise first
+        names = ["quant_x"] + names[:2] + names[3:]
+        fns = [fns[2]] + fns[:2] + fns[3:]
+    return names, fns
+
+
+def time_layer_steps(torch, st, names, fns, cur, steps, warmup):
+    """W untimed steps, then K timed ones with an event pair around every
+    launch on the launch stream and one pair around the whole region.
+    Returns (ms per step, per-kernel mean ms, per-step ms, wall seconds, and
+    the step function itself)."""
+    def step(evs=None):
+        for i, f in enumerate(fns):
+            if evs is not None:
+                evs[i][0].record(st)
+            f()
+            if evs is not None:
+                evs[i][1].record(st)
+        cur["i"] += 1
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in names] for _ in range(steps)]
+    t0 = time.perf_counter()
+    e0.record(st)
+    for i in range(steps):
+        step(evs[i])
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / steps
+    kern = {n: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps)]))
+            for j, n in enumerate(names)}
+    # each step's own time: from the first launch's start event to the last
+    # launch's end event
+    step_ms = [evs[i][0][0].elapsed_time(evs[i][-1][1]) for i in range(steps)]
+    return ms_step, kern, step_ms, wall, step
+
+
+def gemm_work(w):
+    """FLOPs of both expert GEMMs, and the algorithmic HBM bytes of one GEMM1
+    launch (every W1 code and scale once, every token's x codes and scales
+    once, the row map, the h codes and scales out) and of one GEMM2 launch
+    (every W2 code and scale once, the h codes and scales, the expert rows
+    out)."""
+    R, G, T, H, I = w.R, w.G, w.T, w.H, w.I
+    g1_flops = 2.0 * R * H * 2 * I
+    g2_flops = 2.0 * R * I * H
+    g1_bytes = (G * 2 * I * H + G * (2 * I // 128) * (H // 128) * 4
+                + T * H + T * (H // 128) * 4 + R * 4 + (G + 1) * 4
+                + R * I + R * (I // 128) * 4)
+    g2_bytes = (G * H * I + G * (H // 128) * (I // 128) * 4 + R * I + R * (I // 128) * 4
+                + (G + 1) * 4 + R * H * 2)
+    return g1_flops, g2_flops, g1_bytes, g2_bytes
+
+
+def roofline_of(flops, nbytes, ms):
+    """Achieved rate against the binding roof, the one with the longer
+    minimum time (HBM 8 TB/s or FP8 MFMA 5 PFLOP/s)."""
+    t = ms * 1e-3
+    tf, gbs = flops / t / 1e12, nbytes / t / 1e9
+    if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (FP8_PEAK_TFLOPS * 1e12):
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4)}
+    roof.update({"mfma_tflops": round(tf, 2), "mfma_frac": round(tf / FP8_PEAK_TFLOPS, 4),
+                 "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+    return roof
+
+
+def sub_workload(name, args, moe, torch, st, dev, wq):
+    """Another DeepSeek-V3-shaped workload on the same (already quantised)
+    expert weights -- every V3-shaped workload draws its experts from the same
+    generator stream -- timed the same way as the main one: ms and tokens/s
+    per step, both GEMMs against their roofs, and the per-expert load
+    max/mean after each of its batches (one pass from the workload's initial
+    bias, before the timed steps)."""
+    import synth
+    w = synth.WORKLOADS[name]
+
+    def gen(spec, seed=w.seed):
+        t = torch.empty(spec.shape, dtype=torch.bfloat16, device=dev)
+        synth.device_generate(spec, seed, t)
+        return t
+
+    wr = torch.from_numpy(w.router_weight().view(np.int16)).view(torch.bfloat16).to(dev)
+    b0 = torch.from_numpy(w.bias().copy()).to(dev)
+    bias = b0.clone()
+    weights = moe.MoEWeights(wr, bias, w1q=wq[0], w1d=wq[1], w2q=wq[2], w2d=wq[3])
+    lay = moe.MoELayer(weights, w.T, w.k, w.gamma, device=dev)
+    xs = [gen(w.x_spec(b)) for b in range(w.batches)]
+    loads = []
+    for x in xs:
+        lay.forward(x)
+        c = lay.counts.cpu().numpy()
+        loads.append(round(float(c.max() / c.mean()), 3))
+    bias.copy_(b0)
+    cur = {"i": 0}
+    names, fns = layer_step_fns(lay, xs, cur, False)
+    ms_step, kern, step_ms, _, _ = time_layer_steps(torch, st, names, fns, cur, args.steps,
+                                                    args.warmup)
+    g1f, g2f, g1b, g2b = gemm_work(w)
+    tf = (g1f + g2f) / ((kern["gemm1"] + kern["gemm2"]) * 1e-3) / 1e12
+    res = {"config": f"{w.name}: T={w.T} tokens, hidden {w.H}, {w.N} routed experts top-{w.k} "
+                     f"+ 1 shared, SwiGLU intermediate {w.I}"
+                     + (f", {w.batches} batches cycled with sign bias updates" if w.batches > 1
+                        else ""),
+           "T": w.T,
+           "ms_per_step": round(ms_step, 4),
+           "tokens_per_s": round(w.T / (ms_step * 1e-3), 1),
+           "layer_ms_median": round(float(np.median(step_ms)), 4),
+           "gemm_tflops": round(tf, 2),
+           "gemm_frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
+           "gemm1_roofline": dict(roofline_of(g1f, g1b, kern["gemm1"]),
+                                  kernel_avg_ms=round(kern["gemm1"], 4),
+                                  algorithmic_bytes_per_launch=g1b),
+           "gemm2_roofline": dict(roofline_of(g2f, g2b, kern["gemm2"]),
+                                  kernel_avg_ms=round(kern["gemm2"], 4),
+                                  algorithmic_bytes_per_launch=g2b),
+           "kernel_ms": {n: round(v, 4) for n, v in kern.items()},
+           "expert_load_max_over_mean": loads if w.batches > 1 else loads[0]}
+    del lay, xs, weights
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -562,45 +743,9 @@ def main():
     xs = [gen(w.x_spec(b)) for b in range(w.batches)]
     cur = {"i": 0}
 
-    names = ["route", "permute", "quant_x", "gemm1", "gemm2", "combine", "bias"]
-    fns = [lambda: lay.route(xs[cur["i"] % len(xs)]), lay.permute,
-           lambda: lay.quant_x(xs[cur["i"] % len(xs)]), lay.gemm1, lay.gemm2,
-           lay.combine, lay.bias_update]
-    if args.router_fp8:    # the FP8 router reads the quantised x: quantise first
-        names = ["quant_x"] + names[:2] + names[3:]
-        fns = [fns[2]] + fns[:2] + fns[3:]
-
-    def step(evs=None):
-        for i, f in enumerate(fns):
-            if evs is not None:
-                evs[i][0].record(st)
-            f()
-            if evs is not None:
-                evs[i][1].record(st)
-        cur["i"] += 1
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # the timed region: K steps with an event pair around every launch (all
-    # on the launch stream), bracketed by one more pair for the whole region
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in names] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    e0.record(st)
-    for i in range(args.steps):
-        step(evs[i])
-    e1.record(st)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / args.steps
-    per = {n: [evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(args.steps)]
-           for j, n in enumerate(names)}
-    kern = {n: float(np.mean(v)) for n, v in per.items()}
-    # each step's own time: from the first launch's start event to the last
-    # launch's end event
-    step_ms = [evs[i][0][0].elapsed_time(evs[i][-1][1]) for i in range(args.steps)]
+    names, fns = layer_step_fns(lay, xs, cur, args.router_fp8)
+    ms_step, kern, step_ms, wall, step = time_layer_steps(torch, st, names, fns, cur, args.steps,
+                                                          args.warmup)
     # a second pass of K steps, each preceded by a write of flush_mb MiB (not
     # timed) so that no step finds the previous step's data in the caches
     flush = torch.empty(max(args.flush_mb, 1) << 20, dtype=torch.uint8, device=dev)
@@ -663,55 +808,44 @@ def main():
         load_ratio.append(round(float(c.max() / c.mean()), 3))
 
     R, G, T, H, I = w.R, w.G, w.T, w.H, w.I
-    g1_flops = 2.0 * R * H * 2 * I
-    g2_flops = 2.0 * R * I * H
-    # algorithmic HBM bytes of one GEMM1 launch: every W1 code and scale once,
-    # every token's x codes and scales once, the row map, h codes and scales out
-    g1_bytes = (G * 2 * I * H + G * (2 * I // 128) * (H // 128) * 4
-                + T * H + T * (H // 128) * 4 + R * 4 + (G + 1) * 4
-                + R * I + R * (I // 128) * 4)
-    t_g1 = kern["gemm1"] * 1e-3
+    g1_flops, g2_flops, g1_bytes, g2_bytes = gemm_work(w)
     gemm_tflops = (g1_flops + g2_flops) / ((kern["gemm1"] + kern["gemm2"]) * 1e-3) / 1e12
-    g1_tflops = g1_flops / t_g1 / 1e12
-    g1_gbs = g1_bytes / t_g1 / 1e9
-    # the binding roof is the one with the longer minimum time
-    hbm_bound = g1_bytes / (HBM_PEAK_GBS * 1e9) >= g1_flops / (FP8_PEAK_TFLOPS * 1e12)
     tokens_per_s = w.T / (ms_step * 1e-3)
-    if hbm_bound:
-        roof = {"bound": "hbm", "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(g1_gbs / HBM_PEAK_GBS, 4)}
-    else:
-        roof = {"bound": "mfma", "achieved": round(g1_tflops, 2), "peak": FP8_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(g1_tflops / FP8_PEAK_TFLOPS, 4)}
+    r1 = roofline_of(g1_flops, g1_bytes, kern["gemm1"])
+    roof = {k_: r1[k_] for k_ in ("bound", "achieved", "peak", "unit", "frac")}
     roof.update({"traffic": measured_traffic(args.workload),
                  "kernel": "grouped_gemm_kernel<SWIGLU_FP8> (GEMM1)",
                  "kernel_avg_ms": round(kern["gemm1"], 4),
                  "algorithmic_bytes_per_launch": g1_bytes,
-                 "algorithmic_flops_per_launch": g1_flops,
-                 "mfma_tflops": round(g1_tflops, 2),
-                 "mfma_frac": round(g1_tflops / FP8_PEAK_TFLOPS, 4),
-                 "hbm_gbs": round(g1_gbs, 1),
-                 "hbm_frac": round(g1_gbs / HBM_PEAK_GBS, 4)})
+                 "algorithmic_flops_per_launch": g1_flops})
+    roof.update({k_: r1[k_] for k_ in ("mfma_tflops", "mfma_frac", "hbm_gbs", "hbm_frac")})
 
     # the HBM-bound phases: algorithmic bytes (each input read once, each output
     # written once) over the measured kernel time
     N, k = w.N, w.k
-    phase_bytes = {
-        "route": (N * H + (N // 128) * (H // 128) * 4 + T * H + T * (H // 128) * 4
-                  + N * 4 + T * N * 4 + T * k * 8) if args.router_fp8 else
-                 (T * H * 2 + N * H * 2 + N * 4 + T * N * 4 + T * k * 8),
-        "quant_x": T * H * 2 + T * H + T * (H // 128) * 4,
-        "combine": R * H * 2 + T * k * 8 + T * H * 2,
-        "permute": T * k * 4 + N * 4 + (N + 2) * 4 + T * k * 4 + R * 4,
+    # (read, written) algorithmic bytes of each HBM phase
+    phase_rw = {
+        "route": ((N * H + (N // 128) * (H // 128) * 4 + T * H + T * (H // 128) * 4 + N * 4,
+                   T * N * 4 + T * k * 8) if args.router_fp8 else
+                  (T * H * 2 + N * H * 2 + N * 4, T * N * 4 + T * k * 8)),
+        "quant_x": (T * H * 2, T * H + T * (H // 128) * 4),
+        "combine": (R * H * 2 + T * k * 8, T * H * 2),
+        "permute": (T * k * 4, N * 4 + (N + 2) * 4 + T * k * 4 + R * 4),
     }
-    phases = {n: {"bytes": b, "ms": round(kern[n], 4),
-                  "GBps": round(b / (kern[n] * 1e-3) / 1e9, 1),
-                  "hbm_frac": round(b / (kern[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-              for n, b in phase_bytes.items()}
-
     peaks = measured_peaks(moe, torch, st)
-    for ph in phases.values():
-        ph["frac_measured_copy_peak"] = round(ph["GBps"] / peaks["copy_GBps_read_plus_write"], 4)
+    phases = {}
+    for n, (rb, wb) in phase_rw.items():
+        gbs = (rb + wb) / (kern[n] * 1e-3) / 1e9
+        phases[n] = {"bytes": rb + wb, "bytes_read": rb, "bytes_written": wb,
+                     "ms": round(kern[n], 4), "GBps": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "frac_measured_read_write_mix": round(gbs / attainable_GBps(rb, wb, peaks), 4),
+                     "frac_measured_copy_peak": round(gbs / peaks["copy_GBps_read_plus_write"], 4)}
+    # the other DeepSeek-V3-shaped workloads on the same quantised weights
+    subs = {}
+    if args.workload == "prefill" and not args.no_sub_workloads:
+        for sub in ("decode", "skew"):
+            subs[sub] = sub_workload(sub, args, moe, torch, st, dev, (w1q, w1d, w2q, w2d))
     res = {
         "metric": "MoE layer tokens/s + grouped FP8 GEMM TFLOP/s (% peak) at V3 shape, 1 GPU",
         "value": round(tokens_per_s, 1),
@@ -746,6 +880,7 @@ def main():
         "weight_quant_ms": round(t_wq1 + t_wq2, 3),
         "wall_s_timed": round(wall, 3),
     }
+    res.update(subs)
     if args.copy_calibration:
         res["copy_calibration"] = {"bytes_read": peaks["copy_bytes_read"],
                                    "bytes_written": peaks["copy_bytes_written"],

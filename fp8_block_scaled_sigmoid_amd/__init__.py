@@ -86,6 +86,7 @@ def lib():
             "fp8_quant_tokens_128": [_P, _I, _I, _I, _LL, _P, _I, _P, _P, _LL, _P, _P],
             "moe_grouped_wgrad_fp8": [_P, _P, _LL, _I, _P, _P, _LL, _I, _P, _I, _P, _P],
             "moe_probe_fp8_mfma": [_I, _I, _P, _P],
+            "moe_probe_hbm": [_I, _P, ctypes.c_size_t, _P, _P],
             "moe_layer_forward": [ctypes.POINTER(LayerArgs), _P, ctypes.c_size_t, _P],
         }
         for name, args in sig.items():
@@ -394,6 +395,18 @@ def moe_probe_fp8_mfma(blocks, iters, sink=None, stream=None):
     _check("moe_probe_fp8_mfma", lib().moe_probe_fp8_mfma(blocks, iters, _ptr(sink),
                                                           _stream(stream)))
     return sink, float(blocks) * 4 * iters * 16 * 65536
+
+
+def moe_probe_hbm(mode, buf, sink=None, stream=None):
+    """Enqueue the HBM rate probe (a diagnostic, not a layer step): modes 0
+    and 2 read every byte of the device tensor ``buf`` (non-temporal, eight
+    loads in flight per lane; ordinary, four), modes 1 and 3 write them
+    (non-temporal; ordinary stores).  Returns the sink (read modes) or None."""
+    if mode in (0, 2) and sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check("moe_probe_hbm", lib().moe_probe_hbm(mode, _ptr(buf), buf.numel() * buf.element_size(),
+                                                _ptr(sink), _stream(stream)))
+    return sink
 
 
 def moe_layer_workspace_bytes(T, H, N, k, I, with_shared=True):

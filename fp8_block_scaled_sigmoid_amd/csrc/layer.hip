@@ -73,9 +73,10 @@ bool layer_shape_ok(const moe_layer_args& a) {
 bool layer_sizes_supported(const moe_layer_args& a) {
   const long long T = a.T, H = a.H, I = a.I, k = a.k;
   const long long R = T * k + (a.with_shared ? T : 0);
-  // 32-bit in-kernel offsets of the router, the permutation and both GEMMs
-  return T * H * 2 < (1LL << 31) && T * (k + 1) <= 0x7FFFFFFFLL && R * I < (1LL << 31) &&
-         R * H < (1LL << 31);
+  // 32-bit buffer-resource offsets: x (router, quantiser), the permutation's
+  // row numbers and h (GEMM2's A operand).  The expert rows [R, H] are
+  // addressed with 64-bit offsets everywhere (GEMM2 epilogue, combine).
+  return T * H * 2 < (1LL << 31) && T * (k + 1) <= 0x7FFFFFFFLL && R * I < (1LL << 31);
 }
 
 }  // namespace

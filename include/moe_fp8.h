@@ -331,6 +331,22 @@ moe_status_t moe_grouped_wgrad_fp8(const uint8_t* a_q, const float* a_d, long lo
 moe_status_t moe_probe_fp8_mfma(int blocks, int iters, float* sink, hipStream_t stream);
 
 /*
+ * Diagnostic, not a step of the layer: the attainable HBM read and write
+ * rates, so that each bandwidth-bound step can be stated against what the
+ * device delivers for its own mix of reads and writes as well as against the
+ * published peak.  Modes 0 and 2 read all `bytes` of `buf` with 16-byte
+ * loads (0: eight non-temporal loads in flight per lane; 2: four ordinary
+ * ones) and XOR-fold them into *sink (device, caller-owned, one unsigned);
+ * modes 1 and 3 write all `bytes` of `buf` with 16-byte stores (1:
+ * non-temporal; 3: ordinary; sink unused, may be NULL).  The caller times it
+ * (events on `stream`) and takes the faster mode of each kind.  Requires
+ * 0 <= mode <= 3 and bytes % 16 == 0 (MOE_ERR_SHAPE), buf 16-byte aligned
+ * (MOE_ERR_ALIGN), buf non-NULL and, for the read modes, sink non-NULL
+ * (MOE_ERR_NULL).
+ */
+moe_status_t moe_probe_hbm(int mode, void* buf, size_t bytes, unsigned* sink, hipStream_t stream);
+
+/*
  * The whole forward pass of one layer in one call ([TP] section III flowchart
  * and Figure 2; [VE] recipe steps 4-7), enqueued on `stream` in this order:
  *   FP8 router only: fp8_quant_1x128(x) ahead of the routing;
@@ -361,8 +377,9 @@ moe_status_t moe_probe_fp8_mfma(int blocks, int iters, float* sink, hipStream_t 
  * that share a workspace must be ordered on one stream.
  * Requires H % 128 == 0, I % 128 == 0, H, I <= 16384, 16 <= N <= 256,
  * N % 16 == 0 (N % 128 == 0 and N >= 128 with router_fp8), 1 <= k <= min(N, 32),
- * the group conditions of moe_route_topk (MOE_ERR_SHAPE); T * H * 2, R * H
- * and R * I below 2^31 (MOE_ERR_UNSUPPORTED).  Every check runs before the
+ * the group conditions of moe_route_topk (MOE_ERR_SHAPE); T * H * 2 and R * I
+ * below 2^31 (MOE_ERR_UNSUPPORTED; at the DeepSeek-V3 shape, T up to 116508
+ * tokens).  Every check runs before the
  * first launch.
  */
 typedef struct {

@@ -130,6 +130,16 @@ def test_validation_before_any_launch(lib):
     assert lib.moe_probe_fp8_mfma(0, 10, None, None) == 2
     assert lib.moe_probe_fp8_mfma(4, 0, None, None) == 2
     assert lib.moe_probe_fp8_mfma(4, 10, None, None) == 1
+    # the HBM rate probe: mode and size, then pointers, then alignment
+    lib.moe_probe_hbm.argtypes = [I, P, ctypes.c_size_t, P, P]
+    assert lib.moe_probe_hbm(4, dummy, 1024, dummy, None) == 2
+    assert lib.moe_probe_hbm(-1, dummy, 1024, dummy, None) == 2
+    assert lib.moe_probe_hbm(2, dummy, 1024, None, None) == 1
+    assert lib.moe_probe_hbm(0, dummy, 1000, dummy, None) == 2
+    assert lib.moe_probe_hbm(0, None, 1024, dummy, None) == 1
+    assert lib.moe_probe_hbm(0, dummy, 1024, None, None) == 1
+    assert lib.moe_probe_hbm(1, ctypes.c_void_p(8), 1024, None, None) == 3
+    assert lib.moe_probe_hbm(1, dummy, 0, None, None) == 0
     lib.moe_permute_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_permute_workspace_bytes.argtypes = [I, I, I]
     assert lib.moe_permute_workspace_bytes(513, 256, 8) == 3 * 256 * 4
