@@ -87,6 +87,7 @@ def lib():
             "moe_grouped_wgrad_fp8": [_P, _P, _LL, _I, _P, _P, _LL, _I, _P, _I, _P, _P],
             "moe_probe_fp8_mfma": [_I, _I, _P, _P],
             "moe_probe_hbm": [_I, _P, ctypes.c_size_t, _P, _P],
+            "moe_permute_noalloc": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P],
             "moe_layer_forward": [ctypes.POINTER(LayerArgs), _P, ctypes.c_size_t, _P],
         }
         for name, args in sig.items():
@@ -97,6 +98,8 @@ def lib():
         L.moe_permute_workspace_bytes.restype = ctypes.c_size_t
         L.moe_route_workspace_bytes.argtypes = [_I, _I, _I]
         L.moe_route_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_permute_noalloc_max_scratch_bytes.argtypes = []
+        L.moe_permute_noalloc_max_scratch_bytes.restype = ctypes.c_size_t
         L.moe_layer_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
         L.moe_layer_workspace_bytes.restype = ctypes.c_size_t
         L.moe_status_str.argtypes = [_I]
@@ -227,6 +230,23 @@ def moe_permute(idx, N, with_shared=True, out=None, ws=None, stream=None):
                                             _ptr(counts), _ptr(offsets), _ptr(row_of),
                                             _ptr(token_of), _ptr(ws), ws.numel(),
                                             _stream(stream)))
+    return counts, offsets, row_of, token_of
+
+
+def moe_permute_noalloc_max_scratch_bytes():
+    return int(lib().moe_permute_noalloc_max_scratch_bytes())
+
+
+def moe_permute_noalloc(idx, N, with_shared, out, stream=None):
+    """moe_permute without a workspace (the library's own device scratch, for
+    callers that cannot allocate): writes into the caller's ``out`` tensors
+    (counts [N], offsets [N+2], row_of [T,k], token_of [T*k (+T)], int32)."""
+    T, k = idx.shape
+    _dev(idx, torch.int32, "idx")
+    counts, offsets, row_of, token_of = out
+    _check("moe_permute_noalloc", lib().moe_permute_noalloc(
+        _ptr(idx), T, N, k, 1 if with_shared else 0, _ptr(counts), _ptr(offsets), _ptr(row_of),
+        _ptr(token_of), _stream(stream)))
     return counts, offsets, row_of, token_of
 
 

@@ -17,7 +17,17 @@
 // Rows of one group therefore come in token order.  The k experts of a token
 // must be distinct (as top-k makes them); otherwise rows are unspecified but
 // stay in bounds.
+#include <atomic>
+
 #include "common.h"
+
+// The allocation-free variant's scratch: the per-block expert counts of the
+// counting sort, in a file-scope device array of at most kScratchInts ints
+// (1 MiB) that each GPU the library runs on holds until the process ends.
+// Host code never passes the array's name to a kernel: it looks up the
+// array's address on each device once (hipGetSymbolAddress) and uses that.
+constexpr size_t kScratchInts = size_t{1} << 18;
+static __device__ __align__(256) int32_t scratch[kScratchInts];
 
 namespace {
 
@@ -132,19 +142,21 @@ extern "C" size_t moe_permute_workspace_bytes(int T, int N, int k) {
   return blocks * (size_t)N * sizeof(int32_t);
 }
 
-extern "C" moe_status_t moe_permute(const int32_t* topk_idx, int T, int N, int k, int with_shared,
-                                    int32_t* counts, int32_t* offsets, int32_t* row_of,
-                                    int32_t* token_of, void* ws, size_t ws_bytes,
-                                    hipStream_t stream) {
+namespace {
+
+moe_status_t check_permute_args(const int32_t* topk_idx, int T, int N, int k, int32_t* counts,
+                                int32_t* offsets, int32_t* row_of, int32_t* token_of) {
   if (T < 0 || N < 1 || N > kMaxExperts || k < 1 || k > 32) return MOE_ERR_SHAPE;
   if ((long long)T * (k + 1) > 0x7FFFFFFFLL) return MOE_ERR_SHAPE;
   if (!counts || !offsets) return MOE_ERR_NULL;
   if (T > 0 && (!topk_idx || !row_of || !token_of)) return MOE_ERR_NULL;
-  const size_t need = moe_permute_workspace_bytes(T, N, k);
-  if (T > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
-  if (moe_status_t s = check_device()) return s;
+  return MOE_OK;
+}
+
+moe_status_t launch_permute(const int32_t* topk_idx, int T, int N, int k, int with_shared,
+                            int32_t* counts, int32_t* offsets, int32_t* row_of,
+                            int32_t* token_of, int32_t* blk, hipStream_t stream) {
   const int n_blocks = (T + kTokPerBlock - 1) / kTokPerBlock;
-  int32_t* blk = static_cast<int32_t*>(ws);
   if (T > 0)
     hipLaunchKernelGGL(permute_count_kernel, dim3(n_blocks), dim3(256), 0, stream, topk_idx, T, N,
                        k, blk, row_of);
@@ -154,4 +166,63 @@ extern "C" moe_status_t moe_permute(const int32_t* topk_idx, int T, int N, int k
     hipLaunchKernelGGL(permute_scatter_kernel, dim3(n_blocks), dim3(256), 0, stream, topk_idx, T,
                        N, k, with_shared ? 1 : 0, blk, offsets, row_of, token_of);
   return launch_status();
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (devices 0-63; others on every call).
+constexpr int kMaxScratchDevices = 64;
+std::atomic<int32_t*> g_scratch_ptr[kMaxScratchDevices];
+
+moe_status_t scratch_on_device(int32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev >= 0 && dev < kMaxScratchDevices) {
+    if (int32_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire)) {
+      *out = p;
+      return MOE_OK;
+    }
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return hip_fail(e);
+  if (!p) return MOE_ERR_HIP;
+  if (dev >= 0 && dev < kMaxScratchDevices)
+    g_scratch_ptr[dev].store(static_cast<int32_t*>(p), std::memory_order_release);
+  *out = static_cast<int32_t*>(p);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" moe_status_t moe_permute(const int32_t* topk_idx, int T, int N, int k, int with_shared,
+                                    int32_t* counts, int32_t* offsets, int32_t* row_of,
+                                    int32_t* token_of, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  if (moe_status_t s = check_permute_args(topk_idx, T, N, k, counts, offsets, row_of, token_of))
+    return s;
+  const size_t need = moe_permute_workspace_bytes(T, N, k);
+  if (T > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (moe_status_t s = check_device()) return s;
+  return launch_permute(topk_idx, T, N, k, with_shared, counts, offsets, row_of, token_of,
+                        static_cast<int32_t*>(ws), stream);
+}
+
+extern "C" size_t moe_permute_noalloc_max_scratch_bytes(void) {
+  return kScratchInts * sizeof(int32_t);
+}
+
+extern "C" moe_status_t moe_permute_noalloc(const int32_t* topk_idx, int T, int N, int k,
+                                            int with_shared, int32_t* counts, int32_t* offsets,
+                                            int32_t* row_of, int32_t* token_of,
+                                            hipStream_t stream) {
+  if (moe_status_t s = check_permute_args(topk_idx, T, N, k, counts, offsets, row_of, token_of))
+    return s;
+  if (moe_permute_workspace_bytes(T, N, k) > kScratchInts * sizeof(int32_t))
+    return MOE_ERR_UNSUPPORTED;
+  if (moe_status_t s = check_device()) return s;
+  int32_t* blk = nullptr;
+  if (moe_status_t s = scratch_on_device(&blk)) return s;
+  return launch_permute(topk_idx, T, N, k, with_shared, counts, offsets, row_of, token_of, blk,
+                        stream);
 }

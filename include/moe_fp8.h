@@ -146,6 +146,25 @@ moe_status_t moe_permute(const int32_t* topk_idx, int T, int N, int k, int with_
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_permute without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and errors as moe_permute
+ * minus ws/ws_bytes.  Its scratch (the per-block counts of the counting sort,
+ * moe_permute_workspace_bytes(T, N, k) bytes) lives in a device array of the
+ * library of moe_permute_noalloc_max_scratch_bytes() bytes (1 MiB), which
+ * each GPU the library runs on holds until the process ends; larger problems
+ * (e.g. T > 65536 at N = 1024, T > 262144 at N = 256) return
+ * MOE_ERR_UNSUPPORTED and enqueue nothing.  The call allocates nothing; every
+ * call on one GPU shares that GPU's array, so calls that may overlap on one
+ * GPU (on different streams, or from different threads) race and must be
+ * ordered by the caller.  Nothing in the array needs clearing between calls.
+ */
+size_t moe_permute_noalloc_max_scratch_bytes(void);
+moe_status_t moe_permute_noalloc(const int32_t* topk_idx, int T, int N, int k, int with_shared,
+                                 int32_t* counts, int32_t* offsets, int32_t* row_of,
+                                 int32_t* token_of, hipStream_t stream);
+
+/*
  * 1x128 activation quantiser ([TP] section V FP8 detail 1; [DF] "Per-tile FP8
  * scaling").  For each row r and 128-column tile j of x [rows, cols] (row
  * stride ld elements, dtype dt):
