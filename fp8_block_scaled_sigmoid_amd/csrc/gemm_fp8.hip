@@ -19,12 +19,16 @@
 //     (expert); wave (wm, wn) owns 64 rows x 64 columns = 4 x 4 MFMA subtiles,
 //     inside one 128x128 weight block, so it needs one B scale per K block;
 //     its 64 float accumulators stay in VALU registers;
-//   * the A tile (128 rows x 128 B, gathered through a_row_index), the B tile
-//     (256 x 128 B) and the 128 A scales of a K block are copied global -> LDS
-//     by buffer-resource direct-to-LDS loads whose per-lane offset is fixed
-//     and whose K position is the scalar offset, three stages deep: stage
-//     kb + 2 is requested in parts spread over the MFMAs of stage kb, and each
-//     wave waits with an explicit vmcnt for exactly the stage it needs next;
+//   * the A tile (128 rows x 128 B, gathered through a_row_index) and the B
+//     tile (256 x 128 B) of a K block are copied global -> LDS by
+//     buffer-resource direct-to-LDS loads whose per-lane offset is fixed and
+//     whose K position is the scalar offset, three stages deep: stage kb + 2
+//     is requested in parts spread over the MFMAs of stage kb, and each wave
+//     waits with an explicit vmcnt for exactly the stage it needs next; the A
+//     scales come 8 K blocks at a time (a [128 rows][8] window, two windows
+//     double-buffered), one 16-byte copy per lane pair of waves 0-3 riding
+//     with the first stage of each window, so a copy touches 32 rows' cache
+//     lines once per 8 K blocks instead of 64 every K block;
 //   * LDS rows are 128 B; 16-byte chunk c of row r sits at chunk position
 //     c ^ ((r >> 1) & 7), and each direct-to-LDS load writes 1 KiB of
 //     consecutive LDS (8 rows); MFMA lane group lk reads K chunks lk and lk + 4
@@ -68,9 +72,16 @@ constexpr int kMaxGroups = 1025;                        // up to 1024 experts + 
 constexpr int kMaxKb = 128;                             // K <= 16384
 constexpr int kABytes = BM * BK;                        // 16 KiB
 constexpr int kBBytes = BN * BK;                        // 32 KiB
-constexpr int kStage = kABytes + kBBytes + BM * 4;      // + 128 A scales
+constexpr int kStage = kABytes + kBBytes;               // 48 KiB
 constexpr int kStages = 3;
-constexpr int kLds = kStages * kStage;                  // 145.5 KiB
+constexpr int kSWin = 8;                                // K blocks per A-scale window
+constexpr int kSWinBytes = BM * kSWin * 4;              // 4 KiB: [128 rows][8 K blocks]
+constexpr int kSWinOff = kStages * kStage;              // A scales after the ring
+constexpr int kLds = kSWinOff + 2 * kSWinBytes;         // 152 KiB
+// (the single-group K loop keeps the A scales per stage instead, [128] floats
+// in slot kb % 3 of the same area: its reads are four 16-byte loads per K
+// block, where the window's [row][8] layout would take sixteen 4-byte ones)
+constexpr int kSStageBytes = BM * 4;
 
 struct GemmParams {
   const uint8_t* a_q;
@@ -97,6 +108,11 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 }
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// A-scale window slot of a tile row and back (bits 0-1 and 2-3 swapped)
+__device__ __forceinline__ int win_slot(int r) {
+  return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3);
+}
 
 // Direct-to-LDS copies through a buffer resource: the per-lane byte offset is
 // fixed for the whole K loop and the K position is the scalar offset, so
@@ -251,12 +267,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     src = clampi(src, 0, p.a_rows - 1);
     a_off[j] = (int)((long long)src * p.lda) + chunk * 16;
   }
-  int sa_off = 0;
-  if (wave < 2) {
-    const int r = row0 + min(m0 + 64 * wave + lane, rows_g - 1);
+  // A scales.  Ping-pong loop: 8 K blocks at a time (32 contiguous bytes of a
+  // row of a_d): waves 0-3 each load 32 window slots with one 16-byte copy,
+  // lane l filling slot 32 w + l / 2 with K blocks 4 (l & 1) .. + 3 (LDS
+  // [slot][8]).  Slot and row differ by a swap of the two lowest 2-bit fields
+  // (win_slot, its own inverse), so the rows 4 apart that the four MFMA lane
+  // groups read together sit 8 floats apart in LDS, in different banks (in
+  // row order they would be 128 bytes apart, on the same banks).
+  // Single-group loop: waves 0-1 load one K block's scale of 64 rows each
+  // with one 4-byte copy per lane, every K block.
+  int sw_off = 0;
+  if (kPingPong ? wave < 4 : wave < 2) {
+    const int r = kPingPong ? row0 + min(m0 + win_slot(32 * wave + (lane >> 1)), rows_g - 1)
+                            : row0 + min(m0 + 64 * wave + lane, rows_g - 1);
     int src = p.a_row_index ? p.a_row_index[r] : r;
     src = clampi(src, 0, p.a_rows - 1);
-    sa_off = src * nkb_all * 4;
+    sw_off = src * nkb_all * 4 + (kPingPong ? (lane & 1) * 16 : 0);
   }
 #pragma unroll
   for (int hh = 0; hh < kMaxPer; ++hh) {
@@ -292,8 +318,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 #pragma unroll
       for (int j = 2 * part - 2; j < 2 * part; ++j)
         dma16(rs_b, b_off[j], ko, st + kABytes + (8 * j + wave) * 1024);
+    } else if constexpr (kPingPong) {
+      if (wave < 4 && kb % kSWin == 0)
+        dma16(rs_sa, sw_off, kb * 4, smem + kSWinOff + ((kb / kSWin) & 1) * kSWinBytes + wave * 1024);
     } else if (wave < 2) {
-      dma4(rs_sa, sa_off, kb * 4, st + kABytes + kBBytes + wave * 256);
+      dma4(rs_sa, sw_off, kb * 4, smem + kSWinOff + (kb % kStages) * kSStageBytes + wave * 256);
     }
   };
   auto issue = [&](int kb, uint8_t* st) {
@@ -328,8 +357,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   // (the others are padding of a group's last row tile and skip their MFMAs).
   //
   // Two wave groups take turns ("ping-pong"): waves 0-3 and waves 4-7 each
-  // hold one wave per SIMD.  Every K block kb has two phases separated by
-  // workgroup barriers; in each phase one group issues the 16 MFMAs of its
+  // hold one wave per SIMD.  Every K block kb has two phases; in each phase
+  // one group issues the 16 MFMAs of its
   // K block while the other, on the same SIMDs, runs the VALU and memory work:
   // the scale FMAs of its previous MFMAs, its share of the copies of a later
   // stage, and the LDS reads of its next fragments.  So the MFMA pipe and the
@@ -340,11 +369,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   //   phase O_kb: group 1 MFMAs of kb;  group 0 FMAs of kb, copies of stage
   //               kb+3, reads of kb+1.
   // Stage kb (ring slot kb % 3) is read by group 0 in O_kb-1 and by group 1
-  // in E_kb, so its slot is free from O_kb on.
+  // in E_kb, so its slot is free from O_kb on.  Only the end of E_kb is a
+  // workgroup barrier.  The end of O_kb needs none: group 1 may start
+  // E_kb+1 while group 0 is still in O_kb, and what both then do is read
+  // stage kb + 1 (landed at the barrier) and copy into slot kb % 3 (free since
+  // that barrier); the scale window a group-0 copy refills was last read eight
+  // K blocks earlier.
   auto kloop = [&](auto nmi_c) {
     constexpr int NMI = decltype(nmi_c)::value;
     const bool g1 = wave >= 4;
-    const int n_w = wave < 2 ? 7 : 6;          // copies per stage of this wave
+    // copies this wave issues for stage s: 6, plus the scale window (waves 0-3)
+    // when s starts a window
+    auto n_of = [&](int s) { return 6 + ((wave < 4 && s % kSWin == 0) ? 1 : 0); };
     i32x8 af[4], bfr[4];
     f32x4 part[4][4], sc[4];
     float sbv = 0.0f;
@@ -377,11 +413,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     // scale; they are multiplied in the next MFMA phase (scale_rows), so no
     // phase waits for these reads
     auto read_scales = [&](int kb) {
-      const uint8_t* st = smem + (kb % kStages) * kStage;
-      const float* sA = reinterpret_cast<const float*>(st + kABytes + kBBytes) + wm * 64 + 4 * lk;
+      // row wm 64 + mi 16 + 4 lk + v lives in window slot wm 64 + mi 16 + 4 v + lk
+      const float* sA = reinterpret_cast<const float*>(smem + kSWinOff + ((kb / kSWin) & 1) * kSWinBytes) +
+                        (wm * 64 + lk) * kSWin + (kb % kSWin);
       sbv = s_bd[wn >> 1][kb];
 #pragma unroll
-      for (int mi = 0; mi < NMI; ++mi) sc[mi] = *reinterpret_cast<const f32x4*>(sA + mi * 16);
+      for (int mi = 0; mi < NMI; ++mi)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sc[mi][v] = sA[(mi * 16 + 4 * v) * kSWin];
     };
     auto scale_rows = [&]() {
 #pragma unroll
@@ -423,7 +462,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     // registers the FMAs free (nothing in this phase waits for them).
     auto xphase = [&](auto issue_c, auto fma_c, int kb_issue, uint8_t* slot, int kb_read) {
       constexpr bool ISSUE = decltype(issue_c)::value, FMA = decltype(fma_c)::value;
-      if (ISSUE && wave < 2) issue_part(kb_issue, slot, 3);
+      if (ISSUE && wave < 4) issue_part(kb_issue, slot, 3);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (NMI > 0) read_frags(kb_read);
       __builtin_amdgcn_sched_barrier(0);
@@ -447,15 +486,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
       if (kb + 2 >= nkb) {
         wait_and_barrier<0>();
       } else if (kb == 0) {
-        if (n_w == 7) wait_and_barrier<3>(); else wait_and_barrier<2>();
+        wait_and_barrier<2>();
       } else {
-        if (n_w == 7) wait_and_barrier<7>(); else wait_and_barrier<6>();
+        if (n_of(kb + 2) == 7) wait_and_barrier<7>(); else wait_and_barrier<6>();
       }
       __builtin_amdgcn_sched_barrier(0);
     };
     auto end_o = [&]() {
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_barrier" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
     };
     // every wave requests stages 0-2 (the B parts first: they do not wait
@@ -470,9 +507,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
       issue_part(st, smem + st * kStage, 3);
     }
     if (nkb > 2) {
-      if (n_w == 7) wait_and_barrier<6>(); else wait_and_barrier<4>();
+      wait_and_barrier<4>();
     } else if (nkb > 1) {
-      if (n_w == 7) wait_and_barrier<3>(); else wait_and_barrier<2>();
+      wait_and_barrier<2>();
     } else {
       wait_and_barrier<0>();
     }
@@ -560,7 +597,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
       // the same in every subtile: one lane offset per chunk half, and the
       // subtiles sit at constant offsets from it.
       const uint8_t* st = smem + (kb % kStages) * kStage;
-      const float* sA = reinterpret_cast<const float*>(st + kABytes + kBBytes) + wm * 64 + 4 * lk;
+      const float* sA = reinterpret_cast<const float*>(smem + kSWinOff + (kb % kStages) * kSStageBytes) +
+                        wm * 64 + 4 * lk;
       const float sb = s_bd[wn >> 1][kb];
       const uint8_t* a_lo = st + wm * 64 * 128 + frag_lo;
       const uint8_t* a_hi = st + wm * 64 * 128 + frag_hi;
@@ -586,9 +624,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 #pragma unroll
       for (int mi = 1; mi < NMI; ++mi) af[mi] = read_a(mi);
 #pragma unroll
-      for (int mi = 0; mi < NMI; ++mi) sc[mi] = *reinterpret_cast<const f32x4*>(sA + mi * 16);
-#pragma unroll
-      for (int mi = 0; mi < NMI; ++mi) sc[mi] = sc[mi] * sb;
+      for (int mi = 0; mi < NMI; ++mi) sc[mi] = *reinterpret_cast<const f32x4*>(sA + mi * 16) * sb;
       f32x4 part[2][4];
 #pragma unroll
       for (int ni = 0; ni < 5; ++ni) {
