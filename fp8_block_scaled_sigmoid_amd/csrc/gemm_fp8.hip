@@ -82,6 +82,10 @@ constexpr int kLds = kSWinOff + 2 * kSWinBytes;         // 152 KiB
 // in slot kb % 3 of the same area: its reads are four 16-byte loads per K
 // block, where the window's [row][8] layout would take sixteen 4-byte ones)
 constexpr int kSStageBytes = BM * 4;
+// dynamic LDS of each schedule: the ping-pong loop's two windows, or the
+// single-group loop's three per-stage scale slots
+constexpr int kStageSG = kStage + kSStageBytes;          // single-group stage: + its 128 A scales
+constexpr int lds_bytes(bool ping_pong) { return ping_pong ? kSWinOff + 2 * kSWinBytes : kStages * kStageSG; }
 
 struct GemmParams {
   const uint8_t* a_q;
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
       if (wave < 4 && kb % kSWin == 0)
         dma16(rs_sa, sw_off, kb * 4, smem + kSWinOff + ((kb / kSWin) & 1) * kSWinBytes + wave * 1024);
     } else if (wave < 2) {
-      dma4(rs_sa, sw_off, kb * 4, smem + kSWinOff + (kb % kStages) * kSStageBytes + wave * 256);
+      dma4(rs_sa, sw_off, kb * 4, st + kABytes + kBBytes + wave * 256);
     }
   };
   auto issue = [&](int kb, uint8_t* st) {
@@ -579,7 +583,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
       } else {
         wait_and_barrier<0>();
       }
-      uint8_t* st_next = smem + ((kb + 2) % kStages) * kStage;
+      uint8_t* st_next = smem + ((kb + 2) % kStages) * kStageSG;
       if (NMI == 0) {
         if (more) issue(kb + 2, st_next);
         return;
@@ -596,9 +600,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
       // Subtile rows differ by multiples of 16, so a lane's swizzle term is
       // the same in every subtile: one lane offset per chunk half, and the
       // subtiles sit at constant offsets from it.
-      const uint8_t* st = smem + (kb % kStages) * kStage;
-      const float* sA = reinterpret_cast<const float*>(smem + kSWinOff + (kb % kStages) * kSStageBytes) +
-                        wm * 64 + 4 * lk;
+      const uint8_t* st = smem + (kb % kStages) * kStageSG;
+      const float* sA = reinterpret_cast<const float*>(st + kABytes + kBBytes) + wm * 64 + 4 * lk;
       const float sb = s_bd[wn >> 1][kb];
       const uint8_t* a_lo = st + wm * 64 * 128 + frag_lo;
       const uint8_t* a_hi = st + wm * 64 * 128 + frag_hi;
@@ -624,7 +627,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 #pragma unroll
       for (int mi = 1; mi < NMI; ++mi) af[mi] = read_a(mi);
 #pragma unroll
-      for (int mi = 0; mi < NMI; ++mi) sc[mi] = *reinterpret_cast<const f32x4*>(sA + mi * 16) * sb;
+      for (int mi = 0; mi < NMI; ++mi) sc[mi] = *reinterpret_cast<const f32x4*>(sA + mi * 16);
+#pragma unroll
+      for (int mi = 0; mi < NMI; ++mi) sc[mi] = sc[mi] * sb;
       f32x4 part[2][4];
 #pragma unroll
       for (int ni = 0; ni < 5; ++ni) {
@@ -645,7 +650,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
       }
     };
     issue(0, smem);
-    if (nkb > 1) issue(1, smem + kStage);
+    if (nkb > 1) issue(1, smem + kStageSG);
     int kb = 0;
     for (; kb + 2 < nkb; ++kb) kblock(kb, std::true_type{}, std::false_type{});
     if (kb + 1 < nkb) kblock(kb++, std::false_type{}, std::false_type{});
@@ -809,10 +814,10 @@ template <int EPI, bool PING_PONG>
 moe_status_t launch_schedule(const GemmParams& q, long long grid, hipStream_t stream) {
   static std::atomic<uint64_t> lds_set{0};
   if (moe_status_t st = allow_dynamic_lds(
-          reinterpret_cast<const void*>(&grouped_gemm_kernel<EPI, PING_PONG>), kLds, lds_set))
+          reinterpret_cast<const void*>(&grouped_gemm_kernel<EPI, PING_PONG>), lds_bytes(PING_PONG), lds_set))
     return st;
   hipLaunchKernelGGL((grouped_gemm_kernel<EPI, PING_PONG>), dim3((unsigned)grid), dim3(kThreads),
-                     kLds, stream, q);
+                     lds_bytes(PING_PONG), stream, q);
   return launch_status();
 }
 
