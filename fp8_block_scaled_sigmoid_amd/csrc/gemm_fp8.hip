@@ -45,7 +45,7 @@
 //     longer than 2048; the single-group loop for the short ones (GEMM2),
 //     where a workgroup may compute two adjacent column tiles of the same rows
 //     one after the other, the second reusing the group lookup and the row
-//     map;
+//     map, its first stage requested before the first tile's epilogue;
 //   * every workgroup derives the tile list itself from the device-side group
 //     offsets (tiles ordered group, column tile (or pair), row tile), so the
 //     call needs no workspace and no host sync; consecutive row tiles of one
@@ -288,28 +288,38 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     src = clampi(src, 0, p.a_rows - 1);
     sw_off = src * nkb_all * 4 + (kPingPong ? (lane & 1) * 16 : 0);
   }
+  // The B side of column tile n: the block scales of both of its weight
+  // blocks for every K block (into s_bd), its buffer resource and the lanes'
+  // offsets.  Set per column tile; the copy lambdas read them.
+  __amdgpu_buffer_rsrc_t rs_b = make_rsrc(p.b_q, 0);
+  int b_off[4];
+  auto setup_b = [&](int n) {
+    const bool half = p.n_out - n * BN < BN;              // only 128 columns exist
+    for (int i = tid; i < 2 * nkb; i += kThreads) {
+      const int blk = i / nkb, kb = i - blk * nkb;
+      const int nb = min(2 * n + blk, p.n_out / 128 - 1);
+      s_bd[blk][kb] = p.b_d[((long long)g * (p.n_out / 128) + nb) * nkb + kb];
+    }
+    const int b_rows = half ? 128 : BN;
+    rs_b = make_rsrc(p.b_q + ((long long)g * p.n_out + (long long)n * BN) * p.k_dim, b_rows * p.k_dim);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int jj = half ? (j & 1) : j;                  // past n_out: repeat valid rows
+      b_off[j] = (lrow8 + 64 * jj) * p.k_dim + chunk * 16;
+    }
+  };
+  // The single-group schedule with the bf16 epilogue requests the first
+  // stage of a workgroup's second column tile before the first tile's
+  // epilogue, so its latency hides behind it (the epilogue then stages its
+  // output through ring slots 1-2 only).
+  bool prefetched = false;
 #pragma unroll
   for (int hh = 0; hh < kMaxPer; ++hh) {
   if (hh >= n_here) break;
   const int n_tile = per * col + hh;
   const bool half_tile = p.n_out - n_tile * BN < BN;   // only 128 columns exist
   if (hh > 0) __syncthreads();   // the previous tile's epilogue is done with LDS
-
-  // B scales of both weight blocks of this tile, for every K block
-  for (int i = tid; i < 2 * nkb; i += kThreads) {
-    const int blk = i / nkb, kb = i - blk * nkb;
-    const int nb = min(2 * n_tile + blk, p.n_out / 128 - 1);
-    s_bd[blk][kb] = p.b_d[((long long)g * (p.n_out / 128) + nb) * nkb + kb];
-  }
-  const int b_rows = half_tile ? 128 : BN;
-  const __amdgpu_buffer_rsrc_t rs_b =
-      make_rsrc(p.b_q + ((long long)g * p.n_out + (long long)n_tile * BN) * p.k_dim, b_rows * p.k_dim);
-  int b_off[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int jj = half_tile ? (j & 1) : j;             // past n_out: repeat valid rows
-    b_off[j] = (lrow8 + 64 * jj) * p.k_dim + chunk * 16;
-  }
+  if (!prefetched) setup_b(n_tile);
 
   // the copies of one stage, in four parts so they can be spread over a K
   // block's MFMAs: part 0 the A tile, parts 1-2 the B tile, part 3 the A scales
@@ -571,15 +581,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   // for each column subtile issues the 4 MFMAs while the scale FMAs of the
   // previous subtile and one part of the copies of stage kb + 2 run behind
   // them.
-  auto kloop_sg = [&](auto nmi_c) {
+  auto kloop_sg = [&](auto nmi_c, bool pre) {
     constexpr int NMI = decltype(nmi_c)::value;
     // one K block.  MORE: stage kb + 2 exists and is requested meanwhile;
     // LAST: no stage follows this one.
     auto kblock = [&](int kb, auto more_c, auto last_c) {
       constexpr bool more = decltype(more_c)::value, last = decltype(last_c)::value;
-      // stage kb must have landed; stage kb + 1 may still be in flight
+      // stage kb must have landed; stage kb + 1 may still be in flight (and,
+      // when stage 0 was requested before the previous tile's epilogue, that
+      // epilogue's 8 stores, which came between stages 0 and 1)
       if (!last) {
-        if (wave < 2) wait_and_barrier<7>(); else wait_and_barrier<6>();
+        if (pre && kb == 0) {
+          if (wave < 2) wait_and_barrier<15>(); else wait_and_barrier<14>();
+        } else {
+          if (wave < 2) wait_and_barrier<7>(); else wait_and_barrier<6>();
+        }
       } else {
         wait_and_barrier<0>();
       }
@@ -649,7 +665,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
         }
       }
     };
-    issue(0, smem);
+    if (!pre) issue(0, smem);
     if (nkb > 1) issue(1, smem + kStageSG);
     int kb = 0;
     for (; kb + 2 < nkb; ++kb) kblock(kb, std::true_type{}, std::false_type{});
@@ -667,14 +683,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     }
   } else {
     switch (__builtin_amdgcn_readfirstlane(nmi)) {
-      case 4: kloop_sg(std::integral_constant<int, 4>{}); break;
-      case 3: kloop_sg(std::integral_constant<int, 3>{}); break;
-      case 2: kloop_sg(std::integral_constant<int, 2>{}); break;
-      case 1: kloop_sg(std::integral_constant<int, 1>{}); break;
-      default: kloop_sg(std::integral_constant<int, 0>{}); break;
+      case 4: kloop_sg(std::integral_constant<int, 4>{}, prefetched); break;
+      case 3: kloop_sg(std::integral_constant<int, 3>{}, prefetched); break;
+      case 2: kloop_sg(std::integral_constant<int, 2>{}, prefetched); break;
+      case 1: kloop_sg(std::integral_constant<int, 1>{}, prefetched); break;
+      default: kloop_sg(std::integral_constant<int, 0>{}, prefetched); break;
     }
   }
   __syncthreads();   // every wave is done with the stages before they are reused
+  prefetched = false;
+  if constexpr (!kPingPong && EPI == MOE_EPI_BF16) {
+    if (hh + 1 < n_here && !p.row_scale) {
+      setup_b(n_tile + 1);
+      issue(0, smem);
+      prefetched = true;
+    }
+  }
 
   // ---- epilogues.  Lane value (mi, ni, v) sits at tile row
   // wm*64 + mi*16 + 4*lk + v and tile column wn*64 + ni*16 + lrow.
@@ -765,7 +789,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
             *reinterpret_cast<const i32x4*>(otile + row * 128 + c * 16);
     }
   } else if (EPI == MOE_EPI_BF16) {
-    uint16_t* otile = reinterpret_cast<uint16_t*>(smem);   // [128][256] bf16
+    // Staged through ring slots 1-2 (slot 0 may be receiving the next column
+    // tile's first stage).  Every wave issues exactly 8 buffer stores; a lane
+    // whose row or column lies outside the tile points past the buffer's end,
+    // where the store is dropped.
+    uint16_t* otile = reinterpret_cast<uint16_t*>(smem + (kPingPong ? 0 : kStageSG));   // [128][256] bf16
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       if (wm * 64 + mi * 16 >= rows_valid) continue;   // rows that are not stored
@@ -782,14 +810,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
       }
     }
     __syncthreads();
-    uint16_t* out = static_cast<uint16_t*>(p.out);
+    const __amdgpu_buffer_rsrc_t rs_o =
+        make_rsrc(static_cast<uint16_t*>(p.out) + (long long)(row0 + m0) * p.ldo, rows_valid * (int)p.ldo * 2);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int q = tid + kThreads * j;
       const int row = q >> 5, c = q & 31;
-      if (row < rows_valid && n_tile * BN + c * 8 < p.n_out)
-        *reinterpret_cast<i32x4*>(out + (long long)(row0 + m0 + row) * p.ldo + n_tile * BN + c * 8) =
-            *reinterpret_cast<const i32x4*>(otile + row * 256 + c * 8);
+      const int colx = n_tile * BN + c * 8;
+      const int off = colx < p.n_out ? (row * (int)p.ldo + colx) * 2 : 0x7FFFFFF0;
+      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const i32x4*>(otile + row * 256 + c * 8),
+                                             rs_o, off, 0, 0);
     }
   } else {
     float* out = static_cast<float*>(p.out);
