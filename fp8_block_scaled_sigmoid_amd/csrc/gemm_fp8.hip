@@ -891,6 +891,9 @@ extern "C" moe_status_t moe_grouped_gemm_fp8(const moe_gemm_fp8_args* a, hipStre
   if (a->k_dim / BK > kMaxKb) return MOE_ERR_UNSUPPORTED;
   // in-kernel offsets are 32-bit: A must span less than 2 GiB
   if ((long long)a->a_rows * a->lda >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  // the bf16 epilogue stores through a buffer resource over the tile's rows
+  // with 32-bit byte offsets: 128 rows of ldo bf16 must stay below 2^31 bytes
+  if (a->epilogue == MOE_EPI_BF16 && a->ldo > (1 << 22)) return MOE_ERR_UNSUPPORTED;
   if (a->total_rows == 0) return MOE_OK;
   if (a->a_rows == 0) return MOE_ERR_SHAPE;
   if (!a->a_q || !a->a_d || !a->b_q || !a->b_d || !a->group_offsets || !a->out) return MOE_ERR_NULL;

@@ -168,6 +168,9 @@ def test_gemm_validation(lib):
     a.out_d = None
     a.n_out, a.epilogue = 256, 9
     assert lib.moe_grouped_gemm_fp8(ctypes.byref(a), None) == 6
+    a.epilogue, a.ldo = 0, (1 << 22) + 8
+    assert lib.moe_grouped_gemm_fp8(ctypes.byref(a), None) == 6   # bf16 row stride too long
+    a.ldo = 256
     a.epilogue, a.total_rows = 0, 0
     assert lib.moe_grouped_gemm_fp8(ctypes.byref(a), None) == 0   # nothing to do
     a.total_rows, a.epilogue, a.out_d = 8, 1, None
