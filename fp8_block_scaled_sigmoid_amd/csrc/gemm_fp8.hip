@@ -468,22 +468,36 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
           acc[mi][ni][v] = __builtin_fmaf(part[ni][mi][v], sc[mi][v], acc[mi][ni][v]);
       }
     };
-    // The VALU / memory phase, in segments the compiler may not reorder: the
-    // fragment reads of K block kb_read first (their registers are free once
-    // the MFMAs are issued); then eight slices of the scale FMAs with one copy
-    // of a later stage before each of the first six, so the address unit
-    // drains while the FMAs run; last the row scales of kb_read, into the
-    // registers the FMAs free (nothing in this phase waits for them).
+    // The VALU / memory phase, in segments the compiler may not reorder:
+    // eight slices of the scale FMAs, with one copy of a later stage before
+    // each of the first six (so the address unit drains while the FMAs run)
+    // and the fragment reads of K block kb_read spread over the first four
+    // (A and B fragment i in slice i: their registers are free once the
+    // MFMAs are issued; spread out, the LDS queue drains behind the FMAs
+    // instead of stalling the wave, and the last reads still land before the
+    // phase ends); last the row scales of kb_read, into the registers the
+    // FMAs free (nothing in this phase waits for them).
     auto xphase = [&](auto issue_c, auto fma_c, int kb_issue, uint8_t* slot, int kb_read) {
       constexpr bool ISSUE = decltype(issue_c)::value, FMA = decltype(fma_c)::value;
       if (ISSUE && wave < 4) issue_part(kb_issue, slot, 3);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (NMI > 0) read_frags(kb_read);
-      __builtin_amdgcn_sched_barrier(0);
+      const uint8_t* rst = smem + (kb_read % kStages) * kStage;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         if constexpr (ISSUE) {
           if (i < 6) issue_one(kb_issue, slot, i);
+        }
+        if constexpr (NMI > 0) {
+          if (i < 4) {
+            if (i < NMI) {
+              const i32x4 x0 = *reinterpret_cast<const i32x4*>(rst + wm * 64 * 128 + frag_lo + i * 16 * 128);
+              const i32x4 x1 = *reinterpret_cast<const i32x4*>(rst + wm * 64 * 128 + frag_hi + i * 16 * 128);
+              af[i] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            const i32x4 y0 = *reinterpret_cast<const i32x4*>(rst + kABytes + wn * 64 * 128 + frag_lo + i * 16 * 128);
+            const i32x4 y1 = *reinterpret_cast<const i32x4*>(rst + kABytes + wn * 64 * 128 + frag_hi + i * 16 * 128);
+            bfr[i] = __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
         }
         if constexpr (FMA && NMI > 0) fma_pairs(i * 4 * NMI / 8, (i + 1) * 4 * NMI / 8);
         __builtin_amdgcn_sched_barrier(0);
