@@ -608,16 +608,18 @@ def test_gemm_many_groups_bit_exact():
     assert np.array_equal(out.cpu().numpy().astype(np.float64), want)
 
 
-@pytest.mark.parametrize("n_out", [6912, 7040])
-def test_gemm_paired_column_tiles_bit_exact(n_out):
+@pytest.mark.parametrize("n_out,K", [(6912, 128), (7040, 128), (7040, 384)])
+def test_gemm_paired_column_tiles_bit_exact(n_out, K):
     """A grid large enough (about 75 k rows, 27 or 28 column tiles) that the
     bf16 and float32 epilogues compute two column tiles per workgroup; an odd
     count of column tiles (the last pair holds one) and a 128-wide last tile.
-    Integer operands, so every output is exact: sampled rows (every group's
-    first and last rows and ragged tails, and random ones) bit-exact."""
+    With the bf16 epilogue the second tile's first stage is requested before
+    the first tile's epilogue (one K block: the only stage; three: the first
+    wait also counts the epilogue's stores).  Integer operands, so every
+    output is exact: sampled rows (every group's first and last rows and
+    ragged tails, and random ones) bit-exact."""
     moe = _moe()
-    rng = np.random.default_rng(n_out)
-    K = 128
+    rng = np.random.default_rng(n_out + K)
     sizes = [40000, 17, 35000]
     off = _ragged_offsets(sizes)
     R, G = int(off[-1]), len(sizes)
