@@ -78,13 +78,13 @@ constexpr int kSWin = 8;                                // K blocks per A-scale 
 constexpr int kSWinBytes = BM * kSWin * 4;              // 4 KiB: [128 rows][8 K blocks]
 constexpr int kSWinOff = kStages * kStage;              // A scales after the ring
 constexpr int kLds = kSWinOff + 2 * kSWinBytes;         // 152 KiB
-// (the single-group K loop keeps the A scales per stage instead, [128] floats
-// in slot kb % 3 of the same area: its reads are four 16-byte loads per K
-// block, where the window's [row][8] layout would take sixteen 4-byte ones)
+// The single-group K loop keeps one K block's 128 A scales at the end of each
+// of its stages instead: its reads are four 16-byte loads per K block, where
+// the window's [row][8] layout would take sixteen 4-byte ones.
 constexpr int kSStageBytes = BM * 4;
-// dynamic LDS of each schedule: the ping-pong loop's two windows, or the
-// single-group loop's three per-stage scale slots
 constexpr int kStageSG = kStage + kSStageBytes;          // single-group stage: + its 128 A scales
+// dynamic LDS of each schedule: the ring and the two windows, or the ring of
+// single-group stages
 constexpr int lds_bytes(bool ping_pong) { return ping_pong ? kSWinOff + 2 * kSWinBytes : kStages * kStageSG; }
 
 struct GemmParams {
