@@ -79,6 +79,7 @@ def lib():
             "fp8_quant_1x128": [_P, _I, _I, _I, _I, _P, _P, _P],
             "fp8_quant_128x128": [_P, _I, _I, _I, _I, _P, _P, _P],
             "moe_grouped_gemm_fp8": [ctypes.POINTER(GemmArgs), _P],
+            "moe_grouped_gemm_fp8_tiles": [ctypes.POINTER(GemmArgs), _I, _P],
             "moe_combine": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P],
             "moe_bias_update": [_P, _P, _I, _I, _I, ctypes.c_float, _P],
             "moe_seq_balance_loss": [_P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P],
@@ -279,8 +280,11 @@ def fp8_quant_128x128(w, interleave_gate_up=False, q=None, d=None, stream=None):
 
 
 def moe_grouped_gemm_fp8(a_q, a_d, b_q, b_d, group_offsets, total_rows, epilogue,
-                         a_row_index=None, out=None, out_d=None, row_scale=None, stream=None):
-    """Grouped block-scaled FP8 GEMM (see include/moe_fp8.h).  b_q [G, n_out, K]."""
+                         a_row_index=None, out=None, out_d=None, row_scale=None, stream=None,
+                         tile_rows=None):
+    """Grouped block-scaled FP8 GEMM (see include/moe_fp8.h).  b_q [G, n_out, K].
+    tile_rows None calls moe_grouped_gemm_fp8 (the library picks the row tile);
+    0, 128 or 256 calls moe_grouped_gemm_fp8_tiles with it."""
     G, n_out, K = b_q.shape
     dev = a_q.device
     if out is None:
@@ -297,7 +301,11 @@ def moe_grouped_gemm_fp8(a_q, a_d, b_q, b_d, group_offsets, total_rows, epilogue
                     n_out, K, epilogue, out.data_ptr(),
                     out_d.data_ptr() if out_d is not None else None, out.stride(0),
                     row_scale.data_ptr() if row_scale is not None else None)
-    _check("moe_grouped_gemm_fp8", lib().moe_grouped_gemm_fp8(ctypes.byref(args), _stream(stream)))
+    if tile_rows is None:
+        _check("moe_grouped_gemm_fp8", lib().moe_grouped_gemm_fp8(ctypes.byref(args), _stream(stream)))
+    else:
+        _check("moe_grouped_gemm_fp8_tiles",
+               lib().moe_grouped_gemm_fp8_tiles(ctypes.byref(args), int(tile_rows), _stream(stream)))
     return out, out_d
 
 

@@ -854,6 +854,398 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   }
 }
 
+// ---- 256-row tiles for the SwiGLU epilogue ---------------------------------
+// A workgroup of 8 waves computes a 256 x 256 tile (256 rows of one group,
+// one interleaved gate/up block pair); wave (wm, wn) owns rows wm*64..+64 and
+// the 128 columns of weight block wn (0 gate, 1 up): 4 x 8 MFMA subtiles, 128
+// float accumulators.  Per 8.4 MFLOP it moves 16 KiB of A and 16 KiB of B
+// through the compute unit's L1 instead of the 128-row tile's 16 + 32 KiB:
+// each weight line is read once per 256 rows, not twice.
+//   * LDS: two 64 KiB stages (A 256 x 128 B, B 256 x 128 B, rows laid out as
+//     in the 128-row kernel), two A-scale windows [256 slots][8 K blocks] and a
+//     dummy block; 152 KiB.
+//   * Each stage is requested in two parts, by when its slot becomes free.
+//     During K block kb the slot of stage kb holds A (read at the block's
+//     start) and B (read one column subtile at a time).  After a mid-block
+//     barrier (every wave has read A and B rows 0-63 of both weight blocks),
+//     those rows of the slot take stage kb + 2 (the early part: B rows 0-63
+//     and 128-191, A, the scale window); at the start of K block kb + 1 the
+//     rest (B rows 64-127, 192-255) follows.  So one and a half stages are in
+//     flight, which the two-stage ring could not give with whole stages.
+//   * Every stage issues the same number of copies in every wave (the window
+//     copy goes out of range into the dummy block off the first K block of a
+//     window, and the A copies of a 64-row band wholly past the group's end go
+//     out of range), so each wait has a fixed count.
+//   * Inside a column subtile each MFMA is followed by the 4 scale FMAs of the
+//     previous subtile's same row subtile, so the VALU works while the wave's
+//     own MFMAs run (the partials are double-buffered).
+//   * The gate and up waves of a row band are adjacent (wm = (w >> 1) & 3,
+//     wn = w & 1), so they run on different SIMDs (wave w runs on SIMD w % 4)
+//     and a tile with few live rows still uses two SIMDs per band.
+constexpr int BM256 = 256;
+constexpr int kA256 = BM256 * BK;                       // 32 KiB
+constexpr int kStage256 = kA256 + kBBytes;              // 64 KiB
+constexpr int kSWin256 = BM256 * kSWin * 4;             // 8 KiB
+constexpr int kSWinOff256 = 2 * kStage256;              // 128 KiB
+constexpr int kDummy256 = kSWinOff256 + 2 * kSWin256;   // takes the dropped window copies
+constexpr int kLds256 = kDummy256 + 8 * 1024;           // 152 KiB
+
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm256_swiglu_kernel(GemmParams p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int s_tmp[kThreads];
+  __shared__ float s_bd[2][kMaxKb];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = p.G;
+  const int n_tiles = p.n_out / BN;
+  // ---- tile list: as in the 128-row kernel, with 256-row tiles
+  int g, local;
+  {
+    const int per = (G + kThreads - 1) / kThreads;   // <= 3
+    int cnt[3];
+    int run = 0;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int gi = tid * per + i;
+      int c = 0;
+      if (i < per && gi < G) {
+        const int r0 = clampi(p.offsets[gi], 0, p.total_rows);
+        const int r1 = clampi(p.offsets[gi + 1], 0, p.total_rows);
+        const int rows = r1 > r0 ? r1 - r0 : 0;
+        c = ((rows + BM256 - 1) / BM256) * n_tiles;
+      }
+      cnt[i] = c;
+      run += c;
+    }
+    int incl = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) s_tmp[wave] = incl;
+    __syncthreads();
+    int base = incl - run, total = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+      const int t = s_tmp[w];
+      if (w < wave) base += t;
+      total += t;
+    }
+    const int per_xcd = (total + 7) / 8;
+    const int slot = blockIdx.x >> 3, xcd = blockIdx.x & 7;
+    const int L = xcd * per_xcd + slot;
+    if (slot >= per_xcd || L >= total) return;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int gi = tid * per + i;
+      if (i < per && gi < G && L >= base && L < base + cnt[i]) {
+        s_tmp[8] = gi;
+        s_tmp[9] = base;
+      }
+      base += cnt[i];
+    }
+    __syncthreads();
+    g = __builtin_amdgcn_readfirstlane(s_tmp[8]);
+    local = L - s_tmp[9];
+  }
+  const int row0 = clampi(p.offsets[g], 0, p.total_rows);
+  const int rows_g = clampi(p.offsets[g + 1], 0, p.total_rows) - row0;
+  const int mt = (rows_g + BM256 - 1) / BM256;
+  const int n_tile = local / mt;
+  const int m0 = (local - n_tile * mt) * BM256;
+  const int rows_valid = min(BM256, rows_g - m0);
+  const int nkb = p.k_dim / BK;
+
+  // ---- direct-to-LDS sources: copy j of wave w fills rows 64 j + 8 w .. + 7
+  // of the A or B tile (1 KiB), as in the 128-row kernel
+  const int chunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
+  const int lrow8 = 8 * wave + (lane >> 3);
+  const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(p.a_q, (int)(p.a_rows * p.lda));
+  const __amdgpu_buffer_rsrc_t rs_sa = make_rsrc(p.a_d, p.a_rows * nkb * 4);
+  int a_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = row0 + min(m0 + 64 * j + lrow8, rows_g - 1);
+    int src = p.a_row_index ? p.a_row_index[r] : r;
+    src = clampi(src, 0, p.a_rows - 1);
+    a_off[j] = (int)((long long)src * p.lda) + chunk * 16;
+    // a band wholly past the group's end is read by no wave: out of range
+    // (dropped without a fetch; K block offsets stay below 2^14)
+    if (64 * j >= rows_valid) a_off[j] = 0x7FFFFFF0 - 16384;
+  }
+  // A-scale window of 8 K blocks: lane pair (2 s, 2 s + 1) of wave w fills
+  // slot 32 w + s with K blocks 0-3 / 4-7 of row win_slot(32 w + s)
+  int sw_off;
+  {
+    const int r = row0 + min(m0 + win_slot(32 * wave + (lane >> 1)), rows_g - 1);
+    int src = p.a_row_index ? p.a_row_index[r] : r;
+    src = clampi(src, 0, p.a_rows - 1);
+    sw_off = src * nkb * 4 + (lane & 1) * 16;
+  }
+  for (int i = tid; i < 2 * nkb; i += kThreads) {
+    const int blk = i / nkb, kb = i - blk * nkb;
+    s_bd[blk][kb] = p.b_d[((long long)g * (p.n_out / 128) + 2 * n_tile + blk) * nkb + kb];
+  }
+  const __amdgpu_buffer_rsrc_t rs_b =
+      make_rsrc(p.b_q + ((long long)g * p.n_out + (long long)n_tile * BN) * p.k_dim, BN * p.k_dim);
+  const int b_off = lrow8 * p.k_dim + chunk * 16;   // copy j adds 64 j rows in the scalar offset
+
+  auto cp_a = [&](int kb, int j) {
+    dma16(rs_a, a_off[j], kb * BK, smem + (kb & 1) * kStage256 + (8 * j + wave) * 1024);
+  };
+  auto cp_b = [&](int kb, int j) {
+    dma16(rs_b, b_off, kb * BK + 64 * j * p.k_dim, smem + (kb & 1) * kStage256 + kA256 + (8 * j + wave) * 1024);
+  };
+  auto cp_w = [&](int kb) {
+    const bool w = kb % kSWin == 0;
+    dma16(rs_sa, sw_off, w ? kb * 4 : 0x7FFFFFF0,
+          smem + (w ? kSWinOff256 + ((kb / kSWin) & 1) * kSWin256 : kDummy256) + wave * 1024);
+  };
+  // copy i of this wave's share of stage kb: the early part is i 0-6 (B rows
+  // 0-63, B rows 128-191, A 0-3, the window), the late part i 7-8 (B rows
+  // 64-127, 192-255)
+  auto cp = [&](int kb, int i) {
+    if (i == 0) cp_b(kb, 0);
+    else if (i == 1) cp_b(kb, 2);
+    else if (i < 6) cp_a(kb, i - 2);
+    else if (i == 6) cp_w(kb);
+    else if (i == 7) cp_b(kb, 1);
+    else cp_b(kb, 3);
+  };
+
+  const int wm = (wave >> 1) & 3, wn = wave & 1;
+  const int lrow = lane & 15, lk = lane >> 4;
+  const int frag_lo = lrow * 128 + ((lk ^ ((lrow >> 1) & 7)) << 4);
+  const int frag_hi = lrow * 128 + (((lk + 4) ^ ((lrow >> 1) & 7)) << 4);
+  const int wave_rows = rows_valid - wm * 64;
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // The K loop for a wave whose first NMI 16-row subtiles hold valid rows.
+  // NEXT1 / NEXT2: stages kb + 1 / kb + 2 exist (compile-time, so the loop
+  // body has no branch for the compiler to sink the FMAs behind).
+  auto kloop = [&](auto nmi_c) {
+    constexpr int NMI = decltype(nmi_c)::value;
+    auto kblock = [&](int kb, auto next1_c, auto next2_c) {
+      constexpr bool next1 = decltype(next1_c)::value, next2 = decltype(next2_c)::value;
+      // stage kb has landed; the early part of kb + 1 (7 copies) may be in flight
+      if constexpr (next1) wait_and_barrier<7>();
+      else wait_and_barrier<0>();
+      __builtin_amdgcn_sched_barrier(0);
+      const uint8_t* st = smem + (kb & 1) * kStage256;
+      // row wm 64 + mi 16 + 4 lk + v lives in window slot wm 64 + mi 16 + 4 v + lk
+      const float* sA = reinterpret_cast<const float*>(smem + kSWinOff256 + ((kb / kSWin) & 1) * kSWin256) +
+                        (wm * 64 + lk) * kSWin + (kb % kSWin);
+      const float sb = s_bd[wn][kb];
+      const uint8_t* a_lo = st + wm * 64 * 128 + frag_lo;
+      const uint8_t* a_hi = st + wm * 64 * 128 + frag_hi;
+      const uint8_t* b_lo = st + kA256 + wn * 128 * 128 + frag_lo;
+      const uint8_t* b_hi = st + kA256 + wn * 128 * 128 + frag_hi;
+      auto read_b = [&](int ni) {
+        const i32x4 y0 = *reinterpret_cast<const i32x4*>(b_lo + ni * 16 * 128);
+        const i32x4 y1 = *reinterpret_cast<const i32x4*>(b_hi + ni * 16 * 128);
+        return __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      auto read_a = [&](int mi) {
+        const i32x4 x0 = *reinterpret_cast<const i32x4*>(a_lo + mi * 16 * 128);
+        const i32x4 x1 = *reinterpret_cast<const i32x4*>(a_hi + mi * 16 * 128);
+        return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      // the copies issued with column subtile ni: the late part of kb + 1 with
+      // subtiles 0-1 (its rows' slot is free since this block's barrier), the
+      // early part of kb + 2 with subtiles 4-7 (after the mid-block barrier)
+      auto copies_at = [&](int ni) {
+        if (ni < 2) {
+          if (next1) cp(kb + 1, 7 + ni);
+        } else if (ni >= 4 && next2) {
+          if (ni == 4) { cp(kb + 2, 0); cp(kb + 2, 1); }
+          else if (ni == 5) { cp(kb + 2, 2); cp(kb + 2, 3); }
+          else if (ni == 6) { cp(kb + 2, 4); cp(kb + 2, 5); }
+          else cp(kb + 2, 6);
+        }
+      };
+      auto mid_barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      if constexpr (NMI == 0) {
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni) {
+          if (ni == 4) mid_barrier();
+          copies_at(ni);
+        }
+        return;
+      }
+      f32x4 sc[4];
+      i32x8 af[4], bfr[2];
+      af[0] = read_a(0);
+      bfr[0] = read_b(0);
+#pragma unroll
+      for (int mi = 1; mi < NMI; ++mi) af[mi] = read_a(mi);
+#pragma unroll
+      for (int mi = 0; mi < NMI; ++mi)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sc[mi][v] = sA[(mi * 16 + 4 * v) * kSWin];
+#pragma unroll
+      for (int mi = 0; mi < NMI; ++mi) sc[mi] = sc[mi] * sb;
+      f32x4 part[2][4];
+#pragma unroll
+      for (int ni = 0; ni < 9; ++ni) {
+        // every wave's reads of A and of B rows 0-63 of both blocks are done
+        if (ni == 4) mid_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (ni < 7) bfr[(ni + 1) & 1] = read_b(ni + 1);
+        if (ni < 8) copies_at(ni);
+#pragma unroll
+        for (int mi = 0; mi < NMI; ++mi) {
+          if (ni < 8)
+            part[ni & 1][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                af[mi], bfr[ni & 1], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+          if (ni > 0) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              acc[mi][ni - 1][v] = __builtin_fmaf(part[(ni - 1) & 1][mi][v], sc[mi][v], acc[mi][ni - 1][v]);
+          }
+        }
+        // issue order: the next B fragment's reads, the copies, then each
+        // MFMA followed by the previous subtile's 4 FMAs of the same rows
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // vector memory reads
+#pragma unroll
+        for (int mi = 0; mi < NMI; ++mi) {
+          if (ni < 8) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          if (ni > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+        }
+      }
+    };
+    // stage 0 whole, then the early part of stage 1
+#pragma unroll
+    for (int i = 0; i < 9; ++i) cp(0, i);
+    if (nkb > 1) {
+#pragma unroll
+      for (int i = 0; i < 7; ++i) cp(1, i);
+    }
+    constexpr std::true_type yes{};
+    constexpr std::false_type no{};
+    int kb = 0;
+    for (; kb + 2 < nkb; ++kb) kblock(kb, yes, yes);
+    if (kb + 1 < nkb) kblock(kb++, yes, no);
+    kblock(kb, no, no);
+  };
+  switch (__builtin_amdgcn_readfirstlane(clampi((wave_rows + 15) >> 4, 0, 4))) {
+    case 4: kloop(std::integral_constant<int, 4>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    default: kloop(std::integral_constant<int, 0>{}); break;
+  }
+  __syncthreads();   // every wave is done with the stages and windows (no copy is in flight)
+
+  // ---- SwiGLU epilogue.  Lane value (mi, ni, v) sits at tile row
+  // wm*64 + mi*16 + 4*lk + v and column ni*16 + lrow of weight block wn.  The
+  // gate wave keeps columns 0-63 and hands 64-127 to its up partner (wave ^ 1),
+  // which hands back its columns 0-63; each forms h for 64 columns.
+  f32x4* ex = reinterpret_cast<f32x4*>(smem);                          // [8 waves][16][64]
+  float* red = reinterpret_cast<float*>(smem + kSWinOff256);             // [2][256] row maxima
+  float* s_m = reinterpret_cast<float*>(smem + kSWinOff256 + 2048);      // [256] multipliers
+  uint8_t* otile = smem;                                                 // [256][128] codes, after ex
+  const bool gate_wave = wn == 0;
+  const int partner = wave ^ 1;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)   // static indices, element by element: acc stays in registers
+      ex[(wave * 16 + mi * 4 + j) * 64 + lane] =
+          f32x4{gate_wave ? acc[mi][4 + j][0] : acc[mi][j][0], gate_wave ? acc[mi][4 + j][1] : acc[mi][j][1],
+                gate_wave ? acc[mi][4 + j][2] : acc[mi][j][2], gate_wave ? acc[mi][4 + j][3] : acc[mi][j][3]};
+  __syncthreads();
+  float h[4][4][4];
+  uint32_t mxb[16];   // per (mi, v): bits of max |h| over this lane's four columns
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    const bool live = wm * 64 + mi * 16 < rows_valid;   // wave-uniform
+    f32x4 oth[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      oth[j] = live ? ex[(partner * 16 + mi * 4 + j) * 64 + lane] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float mx = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h[mi][j][v] = 0.0f;
+        if (live) {
+          const float mine = gate_wave ? acc[mi][j][v] : acc[mi][4 + j][v];
+          const float other = oth[j][v];
+          const float gt = gate_wave ? mine : other;
+          const float u = gate_wave ? other : mine;
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gt));
+          h[mi][j][v] = gt * sg * u;
+          mx = fmaxf(mx, fabsf(h[mi][j][v]));
+        }
+      }
+      mxb[mi * 4 + v] = __float_as_uint(mx);
+    }
+  }
+  {
+    // lane (lk, lrow) ends with the maximum of row (mi, v) = (lrow / 4, lrow % 4)
+    const uint32_t mx = row_max16_halving(mxb, lrow);
+    red[wn * 256 + wm * 64 + (lrow >> 2) * 16 + 4 * lk + (lrow & 3)] = __uint_as_float(mx);
+  }
+  __syncthreads();
+  // one thread per row forms the tile's scale (two divisions) and stores d
+  const int ld_d = p.n_out / BN;
+  if (tid < BM256) {
+    float m, d;
+    tile_scale(fmaxf(red[tid], red[256 + tid]), m, d);
+    s_m[tid] = m;
+    if (tid < rows_valid) p.out_d[(long long)(row0 + m0 + tid) * ld_d + n_tile] = d;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    if (wm * 64 + mi * 16 >= rows_valid) continue;   // rows that are not stored
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = wm * 64 + mi * 16 + 4 * lk + v;
+      const float m = s_m[row];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) otile[row * 128 + wn * 64 + j * 16 + lrow] = (uint8_t)quant_code(h[mi][j][v], m);
+    }
+  }
+  __syncthreads();
+  uint8_t* out = static_cast<uint8_t*>(p.out);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = tid + kThreads * j;
+    const int row = q >> 3, c = q & 7;
+    if (row < rows_valid)
+      *reinterpret_cast<i32x4*>(out + (long long)(row0 + m0 + row) * p.ldo + n_tile * 128 + c * 16) =
+          *reinterpret_cast<const i32x4*>(otile + row * 128 + c * 16);
+  }
+}
+
+moe_status_t launch256_swiglu(const GemmParams& p, hipStream_t stream) {
+  static std::atomic<uint64_t> lds_set{0};
+  if (moe_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(&grouped_gemm256_swiglu_kernel),
+                                          kLds256, lds_set))
+    return st;
+  const long long n_tiles = p.n_out / BN;
+  const long long row_tiles = (long long)(p.total_rows + BM256 - 1) / BM256 + p.G;   // an upper bound
+  long long grid = row_tiles * n_tiles;
+  grid = (grid + 7) / 8 * 8;
+  if (grid > 0x7FFFFFFFLL) return MOE_ERR_SHAPE;
+  hipLaunchKernelGGL(grouped_gemm256_swiglu_kernel, dim3((unsigned)grid), dim3(kThreads), kLds256, stream, p);
+  return launch_status();
+}
+
 template <int EPI, bool PING_PONG>
 moe_status_t launch_schedule(const GemmParams& q, long long grid, hipStream_t stream) {
   static std::atomic<uint64_t> lds_set{0};
@@ -871,7 +1263,7 @@ moe_status_t launch_schedule(const GemmParams& q, long long grid, hipStream_t st
 // tiles per workgroup as long as the grid still holds at least 32 workgroups
 // per compute unit (so the last, partly filled round stays a small share).
 template <int EPI>
-moe_status_t launch(const GemmParams& p, hipStream_t stream) {
+moe_status_t launch(const GemmParams& p, int tile_rows, hipStream_t stream) {
   const bool ping_pong = EPI == MOE_EPI_SWIGLU_FP8 || p.k_dim / BK > 16;
   const long long n_tiles = (p.n_out + BN - 1) / BN;
   const long long row_tiles = (long long)(p.total_rows + BM - 1) / BM + p.G;   // an upper bound
@@ -884,6 +1276,10 @@ moe_status_t launch(const GemmParams& p, hipStream_t stream) {
   grid = (grid + 7) / 8 * 8;
   if (grid > 0x7FFFFFFFLL) return MOE_ERR_SHAPE;
   if constexpr (EPI == MOE_EPI_SWIGLU_FP8) {
+    // 256-row tiles unless the groups are small (fewer than 128 rows on
+    // average, as in decoding), where a 256-row tile would be mostly padding
+    if (tile_rows == 256 || (tile_rows == 0 && (long long)p.total_rows >= 128LL * p.G))
+      return launch256_swiglu(p, stream);
     return launch_schedule<EPI, true>(q, grid, stream);
   } else {
     return ping_pong ? launch_schedule<EPI, true>(q, grid, stream)
@@ -891,10 +1287,10 @@ moe_status_t launch(const GemmParams& p, hipStream_t stream) {
   }
 }
 
-}  // namespace
-
-extern "C" moe_status_t moe_grouped_gemm_fp8(const moe_gemm_fp8_args* a, hipStream_t stream) {
+moe_status_t grouped_gemm(const moe_gemm_fp8_args* a, int tile_rows, hipStream_t stream) {
   if (!a) return MOE_ERR_NULL;
+  if (tile_rows != 0 && tile_rows != 128 && tile_rows != 256) return MOE_ERR_UNSUPPORTED;
+  if (tile_rows == 256 && a->epilogue != MOE_EPI_SWIGLU_FP8) return MOE_ERR_UNSUPPORTED;
   if (a->num_groups < 1 || a->num_groups > kMaxGroups || a->total_rows < 0 || a->n_out <= 0 ||
       a->k_dim <= 0 || a->k_dim % BK != 0 || a->n_out % 128 != 0 || a->lda < a->k_dim ||
       a->lda % 16 != 0 || a->a_rows < 0)
@@ -925,8 +1321,19 @@ extern "C" moe_status_t moe_grouped_gemm_fp8(const moe_gemm_fp8_args* a, hipStre
   p.n_out = a->n_out; p.k_dim = a->k_dim; p.out = a->out; p.out_d = a->out_d;
   p.ldo = a->ldo; p.row_scale = a->row_scale;
   switch (a->epilogue) {
-    case MOE_EPI_SWIGLU_FP8: return launch<MOE_EPI_SWIGLU_FP8>(p, stream);
-    case MOE_EPI_BF16: return launch<MOE_EPI_BF16>(p, stream);
-    default: return launch<MOE_EPI_F32>(p, stream);
+    case MOE_EPI_SWIGLU_FP8: return launch<MOE_EPI_SWIGLU_FP8>(p, tile_rows, stream);
+    case MOE_EPI_BF16: return launch<MOE_EPI_BF16>(p, tile_rows, stream);
+    default: return launch<MOE_EPI_F32>(p, tile_rows, stream);
   }
+}
+
+}  // namespace
+
+extern "C" moe_status_t moe_grouped_gemm_fp8(const moe_gemm_fp8_args* a, hipStream_t stream) {
+  return grouped_gemm(a, 0, stream);
+}
+
+extern "C" moe_status_t moe_grouped_gemm_fp8_tiles(const moe_gemm_fp8_args* a, int tile_rows,
+                                                   hipStream_t stream) {
+  return grouped_gemm(a, tile_rows, stream);
 }

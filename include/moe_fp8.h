@@ -237,6 +237,21 @@ typedef struct {
 moe_status_t moe_grouped_gemm_fp8(const moe_gemm_fp8_args* args, hipStream_t stream);
 
 /*
+ * The same product with the row tile chosen by the caller (same passages as
+ * above; the result does not depend on the tile: every output is the same
+ * sequence of per-block products and fused multiply-adds).  tile_rows:
+ *   0    as moe_grouped_gemm_fp8: with MOE_EPI_SWIGLU_FP8, 256-row tiles when
+ *        total_rows >= 128 * num_groups, else 128-row tiles;
+ *   128  128-row tiles (every epilogue);
+ *   256  256-row tiles (MOE_EPI_SWIGLU_FP8 only).
+ * Any other value, or 256 with another epilogue, returns MOE_ERR_UNSUPPORTED
+ * before anything is launched.  Arguments, layouts and the other errors are
+ * those of moe_grouped_gemm_fp8.
+ */
+moe_status_t moe_grouped_gemm_fp8_tiles(const moe_gemm_fp8_args* args, int tile_rows,
+                                        hipStream_t stream);
+
+/*
  * Gate-weighted combine ([VE] glossary: routed weights sum to 1 and the shared
  * expert is added at full weight; [TP] Figure 2, outputs "summed into the
  * block output"):

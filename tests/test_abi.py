@@ -32,7 +32,7 @@ def test_header_declares_the_layer_calls():
     for n in ["moe_route_topk", "moe_route_topk_fp8", "moe_route_workspace_bytes",
               "moe_topk_from_scores", "moe_permute",
               "moe_permute_workspace_bytes", "fp8_quant_1x128", "fp8_quant_128x128",
-              "moe_grouped_gemm_fp8", "moe_combine", "moe_bias_update", "moe_status_str",
+              "moe_grouped_gemm_fp8", "moe_grouped_gemm_fp8_tiles", "moe_combine", "moe_bias_update", "moe_status_str",
               "moe_last_hip_error", "fp8_transpose_128x128", "fp8_quant_tokens_128",
               "moe_grouped_wgrad_fp8"]:
         assert n in names, n
@@ -175,6 +175,25 @@ def test_gemm_validation(lib):
     assert lib.moe_grouped_gemm_fp8(ctypes.byref(a), None) == 0   # nothing to do
     a.total_rows, a.epilogue, a.out_d = 8, 1, None
     assert lib.moe_grouped_gemm_fp8(ctypes.byref(a), None) == 1   # SwiGLU needs out_d
+
+
+def test_gemm_tiles_validation(lib):
+    f = lib.moe_grouped_gemm_fp8_tiles
+    f.argtypes = [ctypes.POINTER(GemmArgs), ctypes.c_int, ctypes.c_void_p]
+    assert f(None, 0, None) == 1
+    a = GemmArgs(16, 16, 256, 8, None, 16, 16, 16, 3, 8, 256, 256, 0, 16, None, 256, None)
+    for bad in (-1, 1, 64, 192, 512):
+        assert f(ctypes.byref(a), bad, None) == 6, bad          # no such row tile
+    assert f(ctypes.byref(a), 256, None) == 6                   # 256 rows: SwiGLU only
+    a.epilogue = 2
+    assert f(ctypes.byref(a), 256, None) == 6
+    a.epilogue, a.out_d = 1, None
+    for t in (0, 128, 256):
+        assert f(ctypes.byref(a), t, None) == 1, t              # the other checks still apply
+    a.out_d, a.n_out = 16, 384
+    assert f(ctypes.byref(a), 256, None) == 2                   # n_out % 256
+    a.n_out, a.total_rows = 256, 0
+    assert f(ctypes.byref(a), 256, None) == 0                   # nothing to do
 
 
 def _layer_args(**kw):

@@ -711,11 +711,11 @@ def test_gemm_single_group_against_library_matmul(K):
     assert ratio <= 2e-4
 
 
-def _swiglu_case(integer):
+def _swiglu_case(integer, tile_rows=None):
     moe = _moe()
     rng = np.random.default_rng(12)
     H, I = 512, 256
-    sizes = [40, 0, 130, 7, 64, 20, 192]
+    sizes = [40, 0, 130, 7, 64, 20, 192, 257, 513]
     off = _ragged_offsets(sizes)
     R, G = int(off[-1]), len(sizes)
     T = 50
@@ -737,22 +737,24 @@ def _swiglu_case(integer):
         w1q_nat, w1d_nat = quant.quant_128x128(synth.as_f64(w1))
         w1q_dev, w1d_dev = moe.fp8_quant_128x128(bf16_to_dev(w1), interleave_gate_up=True)
     tok = rng.integers(0, T, R).astype(np.int32)
-    log(f"moe_grouped_gemm_fp8 swiglu integer={integer}")
+    log(f"moe_grouped_gemm_fp8 swiglu integer={integer} tile_rows={tile_rows}")
     hq, hd = moe.moe_grouped_gemm_fp8(to_dev(xq), to_dev(xd), w1q_dev, w1d_dev, to_dev(off), R,
-                                      moe.MOE_EPI_SWIGLU_FP8, a_row_index=to_dev(tok))
+                                      moe.MOE_EPI_SWIGLU_FP8, a_row_index=to_dev(tok),
+                                      tile_rows=tile_rows)
     torch.cuda.synchronize()
     return hq.cpu().numpy(), hd.cpu().numpy(), xq, xd, w1q_nat, w1d_nat, tok, off, I
 
 
+@pytest.mark.parametrize("tile_rows", [128, 256])
 @pytest.mark.parametrize("integer", [True, False])
-def test_gemm_swiglu_epilogue(integer):
+def test_gemm_swiglu_epilogue(integer, tile_rows):
     """Integer operands: a is exact on both sides, so codes must match except
     within 2e-6 of a rounding tie and the scales to 1e-6.  Random operands: a
     carries the MFMA block-sum error, so h is checked against the oracle with
     the per-element band propagated from that bound (check_h): scales and
     dequantised values inside it, differing codes only at rounding midpoints
     inside it and roundings of values inside it, and at most flip_cap of them."""
-    hq, hd, xq, xd, w1q_nat, w1d_nat, tok, off, I = _swiglu_case(integer)
+    hq, hd, xq, xd, w1q_nat, w1d_nat, tok, off, I = _swiglu_case(integer, tile_rows)
     n_diff, n_all = 0, 0
     for g in range(len(off) - 1):
         rr = np.arange(off[g], off[g + 1])
@@ -775,6 +777,40 @@ def test_gemm_swiglu_epilogue(integer):
         assert n_diff <= 1e-4 * n_all
     else:
         assert n_diff <= flip_cap(n_all)
+
+
+@pytest.mark.parametrize("K", [128, 256, 384, 1152, 2176])
+def test_gemm_swiglu_tile_sizes_agree_bit_exact(K):
+    """The 256-row and the 128-row SwiGLU kernels form every output from the
+    same sequence of per-block MFMA products and fused multiply-adds, then the
+    same float32 epilogue, so their codes and scales must be identical bit for
+    bit.  Group sizes straddle both tile heights (empty, 1, 255-257, 511-513,
+    rows past a 64-row band), and K covers 1, 2 and 3 K blocks (the prologue
+    and the loop's tail) and 9 and 17 (past one and two 8-block scale
+    windows); the A rows are gathered through a random index."""
+    moe = _moe()
+    rng = np.random.default_rng(1000 + K)
+    I = 256
+    sizes = [1, 0, 255, 256, 257, 300, 17, 511, 512, 513, 64, 65, 129, 0, 3]
+    off = _ragged_offsets(sizes)
+    R, G = int(off[-1]), len(sizes)
+    T = 700
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+    xq, xd = moe.fp8_quant_1x128(bf16_to_dev(xb))
+    w1 = synth.f32_to_bf16_bits((rng.standard_normal((G, 2 * I, K)) * 0.03).astype(np.float32))
+    w1q, w1d = moe.fp8_quant_128x128(bf16_to_dev(w1), interleave_gate_up=True)
+    tok = to_dev(rng.integers(0, T, R).astype(np.int32))
+    got = {}
+    for t in (128, 256, 0):
+        log(f"moe_grouped_gemm_fp8_tiles swiglu K={K} tile_rows={t}")
+        hq, hd = moe.moe_grouped_gemm_fp8(xq, xd, w1q, w1d, to_dev(off), R, moe.MOE_EPI_SWIGLU_FP8,
+                                          a_row_index=tok, tile_rows=t)
+        torch.cuda.synchronize()
+        got[t] = (hq.cpu().numpy(), hd.cpu().numpy())
+    for t in (256, 0):
+        np.testing.assert_array_equal(got[t][0], got[128][0])
+        np.testing.assert_array_equal(got[t][1].view(np.uint32), got[128][1].view(np.uint32))
+    assert np.count_nonzero(got[128][0]) > R * I // 4      # the outputs carry data
 
 
 def _gpu_silu_rel_bound(g):
