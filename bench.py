@@ -828,7 +828,7 @@ def main():
     r1 = roofline_of(g1_flops, g1_bytes, kern["gemm1"])
     roof = {k_: r1[k_] for k_ in ("bound", "achieved", "peak", "unit", "frac")}
     roof.update({"traffic": measured_traffic(args.workload),
-                 "kernel": "grouped_gemm_kernel<SWIGLU_FP8> (GEMM1)",
+                 "kernel": "grouped_gemm256_swiglu_kernel (GEMM1, 256-row tiles)",
                  "kernel_avg_ms": round(kern["gemm1"], 4),
                  "algorithmic_bytes_per_launch": g1_bytes,
                  "algorithmic_flops_per_launch": g1_flops})
