@@ -1156,49 +1156,55 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm256_swiglu_kernel(Gem
   float* red = reinterpret_cast<float*>(smem + kSWinOff256);             // [2][256] row maxima
   float* s_m = reinterpret_cast<float*>(smem + kSWinOff256 + 2048);      // [256] multipliers
   uint8_t* otile = smem;                                                 // [256][128] codes, after ex
-  const bool gate_wave = wn == 0;
   const int partner = wave ^ 1;
+  // The gate / up role is fixed per wave, so each phase is compiled for both
+  // roles and a wave-uniform branch picks one (a role chosen per element
+  // costs a select and register moves for each of the 128 values); the
+  // barriers stay outside the branches.
+  auto hand_over = [&](auto gate_c) {
+    constexpr bool GATE = decltype(gate_c)::value;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)   // static indices, element by element: acc stays in registers
-      ex[(wave * 16 + mi * 4 + j) * 64 + lane] =
-          f32x4{gate_wave ? acc[mi][4 + j][0] : acc[mi][j][0], gate_wave ? acc[mi][4 + j][1] : acc[mi][j][1],
-                gate_wave ? acc[mi][4 + j][2] : acc[mi][j][2], gate_wave ? acc[mi][4 + j][3] : acc[mi][j][3]};
+      for (int j = 0; j < 4; ++j) ex[(wave * 16 + mi * 4 + j) * 64 + lane] = GATE ? acc[mi][4 + j] : acc[mi][j];
+  };
+  if (wn == 0) hand_over(std::true_type{});
+  else hand_over(std::false_type{});
   __syncthreads();
+  // Subtiles past the group's end had no MFMAs, so both partners' values
+  // there are +0 and h is +0: every row is formed without a branch, the row
+  // maxima of stored rows are unchanged, and those rows are never stored.
   float h[4][4][4];
-  uint32_t mxb[16];   // per (mi, v): bits of max |h| over this lane's four columns
+  auto form_h = [&](auto gate_c) {
+    constexpr bool GATE = decltype(gate_c)::value;
+    uint32_t mxb[16];   // per (mi, v): bits of max |h| over this lane's four columns
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    const bool live = wm * 64 + mi * 16 < rows_valid;   // wave-uniform
-    f32x4 oth[4];
+    for (int mi = 0; mi < 4; ++mi) {
+      f32x4 oth[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      oth[j] = live ? ex[(partner * 16 + mi * 4 + j) * 64 + lane] : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 4; ++j) oth[j] = ex[(partner * 16 + mi * 4 + j) * 64 + lane];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float mx = 0.0f;
+      for (int v = 0; v < 4; ++v) {
+        float mx = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        h[mi][j][v] = 0.0f;
-        if (live) {
-          const float mine = gate_wave ? acc[mi][j][v] : acc[mi][4 + j][v];
+        for (int j = 0; j < 4; ++j) {
+          const float mine = GATE ? acc[mi][j][v] : acc[mi][4 + j][v];
           const float other = oth[j][v];
-          const float gt = gate_wave ? mine : other;
-          const float u = gate_wave ? other : mine;
+          const float gt = GATE ? mine : other;
+          const float u = GATE ? other : mine;
           const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gt));
           h[mi][j][v] = gt * sg * u;
           mx = fmaxf(mx, fabsf(h[mi][j][v]));
         }
+        mxb[mi * 4 + v] = __float_as_uint(mx);
       }
-      mxb[mi * 4 + v] = __float_as_uint(mx);
     }
-  }
-  {
     // lane (lk, lrow) ends with the maximum of row (mi, v) = (lrow / 4, lrow % 4)
     const uint32_t mx = row_max16_halving(mxb, lrow);
     red[wn * 256 + wm * 64 + (lrow >> 2) * 16 + 4 * lk + (lrow & 3)] = __uint_as_float(mx);
-  }
+  };
+  if (wn == 0) form_h(std::true_type{});
+  else form_h(std::false_type{});
   __syncthreads();
   // one thread per row forms the tile's scale (two divisions) and stores d
   const int ld_d = p.n_out / BN;
@@ -1211,7 +1217,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm256_swiglu_kernel(Gem
   __syncthreads();
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
-    if (wm * 64 + mi * 16 >= rows_valid) continue;   // rows that are not stored
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int row = wm * 64 + mi * 16 + 4 * lk + v;
