@@ -952,10 +952,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm256_swiglu_kernel(Gem
   }
   const int row0 = clampi(p.offsets[g], 0, p.total_rows);
   const int rows_g = clampi(p.offsets[g + 1], 0, p.total_rows) - row0;
+  // A group's rows are split evenly over its ceil(rows / 256) row tiles (291
+  // rows: 146 + 145, not 256 + 35).  The row tiles of one weight tile run
+  // side by side on one XCD and share its lines in L2 only while they stay in
+  // step; a nearly empty last tile would run ahead and fetch them again.
   const int mt = (rows_g + BM256 - 1) / BM256;
   const int n_tile = local / mt;
-  const int m0 = (local - n_tile * mt) * BM256;
-  const int rows_valid = min(BM256, rows_g - m0);
+  const int rt = local - n_tile * mt;
+  const int m0 = (int)((long long)rt * rows_g / mt);
+  const int rows_valid = (int)((long long)(rt + 1) * rows_g / mt) - m0;   // <= 256
   const int nkb = p.k_dim / BK;
 
   // ---- direct-to-LDS sources: copy j of wave w fills rows 64 j + 8 w .. + 7
