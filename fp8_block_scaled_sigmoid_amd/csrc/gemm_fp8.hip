@@ -854,7 +854,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   }
 }
 
-// ---- 256-row tiles for the SwiGLU epilogue ---------------------------------
+// ---- 256-row tiles for the SwiGLU and bf16 epilogues -----------------------
 // A workgroup of 8 waves computes a 256 x 256 tile (256 rows of one group,
 // one interleaved gate/up block pair); wave (wm, wn) owns rows wm*64..+64 and
 // the 128 columns of weight block wn (0 gate, 1 up): 4 x 8 MFMA subtiles, 128
@@ -890,7 +890,8 @@ constexpr int kSWinOff256 = 2 * kStage256;              // 128 KiB
 constexpr int kDummy256 = kSWinOff256 + 2 * kSWin256;   // takes the dropped window copies
 constexpr int kLds256 = kDummy256 + 8 * 1024;           // 152 KiB
 
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm256_swiglu_kernel(GemmParams p) {
+template <int EPI>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm256_kernel(GemmParams p) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int s_tmp[kThreads];
   __shared__ float s_bd[2][kMaxKb];
@@ -1153,6 +1154,39 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm256_swiglu_kernel(Gem
   }
   __syncthreads();   // every wave is done with the stages and windows (no copy is in flight)
 
+  if constexpr (EPI == MOE_EPI_BF16) {
+    // ---- bf16 epilogue: staged through LDS ([256][256] bf16 over both stage
+    // slots), then 16 coalesced 16-byte buffer stores per thread; a row past
+    // the tile's valid rows points past the buffer's end, where the store is
+    // dropped.  Lane value (mi, ni, v) sits at tile row wm*64 + mi*16 + 4*lk + v
+    // and column wn*128 + ni*16 + lrow.
+    uint16_t* otile = reinterpret_cast<uint16_t*>(smem);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = wm * 64 + mi * 16 + 4 * lk + v;
+        float rs = 1.0f;
+        if (p.row_scale) rs = p.row_scale[row0 + min(m0 + row, rows_g - 1)];
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni) {
+          const float val = p.row_scale ? acc[mi][ni][v] * rs : acc[mi][ni][v];
+          otile[row * 256 + wn * 128 + ni * 16 + lrow] = (uint16_t)f32_to_bf16(val);
+        }
+      }
+    __syncthreads();
+    // 256 rows of ldo <= 2^21 bf16: the resource and every offset stay below 2^31
+    const __amdgpu_buffer_rsrc_t rs_o =
+        make_rsrc(static_cast<uint16_t*>(p.out) + (long long)(row0 + m0) * p.ldo, rows_valid * (int)p.ldo * 2);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int q = tid + kThreads * j;
+      const int row = q >> 5, c = q & 31;
+      const int off = row < rows_valid ? (row * (int)p.ldo + n_tile * BN + c * 8) * 2 : 0x7FFFFFF0;
+      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const i32x4*>(otile + row * 256 + c * 8), rs_o,
+                                             off, 0, 0);
+    }
+  } else {
   // ---- SwiGLU epilogue.  Lane value (mi, ni, v) sits at tile row
   // wm*64 + mi*16 + 4*lk + v and column ni*16 + lrow of weight block wn.  The
   // gate wave keeps columns 0-63 and hands 64-127 to its up partner (wave ^ 1),
@@ -1240,11 +1274,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm256_swiglu_kernel(Gem
       *reinterpret_cast<i32x4*>(out + (long long)(row0 + m0 + row) * p.ldo + n_tile * 128 + c * 16) =
           *reinterpret_cast<const i32x4*>(otile + row * 128 + c * 16);
   }
+  }
 }
 
-moe_status_t launch256_swiglu(const GemmParams& p, hipStream_t stream) {
+template <int EPI>
+moe_status_t launch256(const GemmParams& p, hipStream_t stream) {
   static std::atomic<uint64_t> lds_set{0};
-  if (moe_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(&grouped_gemm256_swiglu_kernel),
+  if (moe_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(&grouped_gemm256_kernel<EPI>),
                                           kLds256, lds_set))
     return st;
   const long long n_tiles = p.n_out / BN;
@@ -1252,7 +1288,7 @@ moe_status_t launch256_swiglu(const GemmParams& p, hipStream_t stream) {
   long long grid = row_tiles * n_tiles;
   grid = (grid + 7) / 8 * 8;
   if (grid > 0x7FFFFFFFLL) return MOE_ERR_SHAPE;
-  hipLaunchKernelGGL(grouped_gemm256_swiglu_kernel, dim3((unsigned)grid), dim3(kThreads), kLds256, stream, p);
+  hipLaunchKernelGGL(grouped_gemm256_kernel<EPI>, dim3((unsigned)grid), dim3(kThreads), kLds256, stream, p);
   return launch_status();
 }
 
@@ -1285,11 +1321,16 @@ moe_status_t launch(const GemmParams& p, int tile_rows, hipStream_t stream) {
   long long grid = row_tiles * n_cols;
   grid = (grid + 7) / 8 * 8;
   if (grid > 0x7FFFFFFFLL) return MOE_ERR_SHAPE;
+  // 256-row tiles (SwiGLU and bf16 epilogues) unless the groups are small
+  // (fewer than 128 rows on average, as in decoding), where a 256-row tile
+  // would be mostly padding; the bf16 one also needs whole 256-column tiles
+  // and ldo <= 2^21 (its store offsets over 256 rows are 32-bit)
+  if constexpr (EPI != MOE_EPI_F32) {
+    const bool fits = EPI == MOE_EPI_SWIGLU_FP8 || (p.n_out % BN == 0 && p.ldo <= (1 << 21));
+    if (tile_rows == 256 || (tile_rows == 0 && fits && (long long)p.total_rows >= 128LL * p.G))
+      return launch256<EPI>(p, stream);
+  }
   if constexpr (EPI == MOE_EPI_SWIGLU_FP8) {
-    // 256-row tiles unless the groups are small (fewer than 128 rows on
-    // average, as in decoding), where a 256-row tile would be mostly padding
-    if (tile_rows == 256 || (tile_rows == 0 && (long long)p.total_rows >= 128LL * p.G))
-      return launch256_swiglu(p, stream);
     return launch_schedule<EPI, true>(q, grid, stream);
   } else {
     return ping_pong ? launch_schedule<EPI, true>(q, grid, stream)
@@ -1300,7 +1341,9 @@ moe_status_t launch(const GemmParams& p, int tile_rows, hipStream_t stream) {
 moe_status_t grouped_gemm(const moe_gemm_fp8_args* a, int tile_rows, hipStream_t stream) {
   if (!a) return MOE_ERR_NULL;
   if (tile_rows != 0 && tile_rows != 128 && tile_rows != 256) return MOE_ERR_UNSUPPORTED;
-  if (tile_rows == 256 && a->epilogue != MOE_EPI_SWIGLU_FP8) return MOE_ERR_UNSUPPORTED;
+  if (tile_rows == 256 && a->epilogue == MOE_EPI_F32) return MOE_ERR_UNSUPPORTED;
+  if (tile_rows == 256 && a->epilogue == MOE_EPI_BF16 && (a->n_out % BN != 0 || a->ldo > (1 << 21)))
+    return MOE_ERR_UNSUPPORTED;
   if (a->num_groups < 1 || a->num_groups > kMaxGroups || a->total_rows < 0 || a->n_out <= 0 ||
       a->k_dim <= 0 || a->k_dim % BK != 0 || a->n_out % 128 != 0 || a->lda < a->k_dim ||
       a->lda % 16 != 0 || a->a_rows < 0)

@@ -240,12 +240,14 @@ moe_status_t moe_grouped_gemm_fp8(const moe_gemm_fp8_args* args, hipStream_t str
  * The same product with the row tile chosen by the caller (same passages as
  * above; the result does not depend on the tile: every output is the same
  * sequence of per-block products and fused multiply-adds).  tile_rows:
- *   0    as moe_grouped_gemm_fp8: with MOE_EPI_SWIGLU_FP8, 256-row tiles when
- *        total_rows >= 128 * num_groups, else 128-row tiles;
+ *   0    as moe_grouped_gemm_fp8: 256-row tiles when total_rows >= 128 *
+ *        num_groups for MOE_EPI_SWIGLU_FP8, and for MOE_EPI_BF16 when also
+ *        n_out % 256 == 0 and ldo <= 2^21; else 128-row tiles;
  *   128  128-row tiles (every epilogue);
- *   256  256-row tiles (MOE_EPI_SWIGLU_FP8 only).
- * Any other value, or 256 with another epilogue, returns MOE_ERR_UNSUPPORTED
- * before anything is launched.  Arguments, layouts and the other errors are
+ *   256  256-row tiles (MOE_EPI_SWIGLU_FP8; MOE_EPI_BF16 with n_out % 256 == 0
+ *        and ldo <= 2^21).
+ * Any other value, or 256 where it is not allowed, returns
+ * MOE_ERR_UNSUPPORTED before anything is launched.  Arguments, layouts and the other errors are
  * those of moe_grouped_gemm_fp8.
  */
 moe_status_t moe_grouped_gemm_fp8_tiles(const moe_gemm_fp8_args* args, int tile_rows,

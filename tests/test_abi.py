@@ -184,9 +184,13 @@ def test_gemm_tiles_validation(lib):
     a = GemmArgs(16, 16, 256, 8, None, 16, 16, 16, 3, 8, 256, 256, 0, 16, None, 256, None)
     for bad in (-1, 1, 64, 192, 512):
         assert f(ctypes.byref(a), bad, None) == 6, bad          # no such row tile
-    assert f(ctypes.byref(a), 256, None) == 6                   # 256 rows: SwiGLU only
     a.epilogue = 2
-    assert f(ctypes.byref(a), 256, None) == 6
+    assert f(ctypes.byref(a), 256, None) == 6                   # 256 rows: not with float32 out
+    a.epilogue, a.n_out = 0, 384
+    assert f(ctypes.byref(a), 256, None) == 6                   # bf16 256 rows: n_out % 256
+    a.n_out, a.ldo = 256, (1 << 21) + 8
+    assert f(ctypes.byref(a), 256, None) == 6                   # bf16 256 rows: ldo <= 2^21
+    a.ldo = 256
     a.epilogue, a.out_d = 1, None
     for t in (0, 128, 256):
         assert f(ctypes.byref(a), t, None) == 1, t              # the other checks still apply

@@ -477,6 +477,7 @@ def _int_codes(rng, shape, lim=4):
     (7168, 512, [5, 0, 200], True),
     (2048, 7168, [130, 3], False),
     (16384, 256, [3, 130], True),               # the largest K: 128 K blocks
+    (1152, 512, [255, 256, 257, 600, 0, 31], True),   # 256-row tiles: evenly split groups
 ])
 def test_gemm_integer_operands_bit_exact(K, n_out, sizes, gather):
     """Integer-valued codes with power-of-two scales: every partial sum is an
@@ -497,28 +498,34 @@ def test_gemm_integer_operands_bit_exact(K, n_out, sizes, gather):
         rr = np.arange(off[g], off[g + 1])
         if rr.size:
             want[rr] = ffn.block_scaled_gemm(aq[src[rr]], ad[src[rr]], bq[g], bd[g])
-    for epi in (moe.MOE_EPI_F32, moe.MOE_EPI_BF16):
-        log(f"moe_grouped_gemm_fp8 integer K={K} n_out={n_out} sizes={sizes} epi={epi}")
+    # the bf16 epilogue on both row tiles where the columns allow 256-row tiles
+    runs = [(moe.MOE_EPI_F32, None)] + [(moe.MOE_EPI_BF16, t) for t in
+                                        ((128, 256) if n_out % 256 == 0 else (None,))]
+    for epi, tile_rows in runs:
+        log(f"moe_grouped_gemm_fp8 integer K={K} n_out={n_out} sizes={sizes} epi={epi} tile_rows={tile_rows}")
         out, _ = moe.moe_grouped_gemm_fp8(to_dev(aq), to_dev(ad), to_dev(bq), to_dev(bd),
                                           to_dev(off), R, epi,
-                                          a_row_index=to_dev(rix) if gather else None)
+                                          a_row_index=to_dev(rix) if gather else None,
+                                          tile_rows=tile_rows)
         torch.cuda.synchronize()
         got = out.float().cpu().numpy().astype(np.float64)
         ref = want if epi == moe.MOE_EPI_F32 else ffn.bf16_round(want)
         assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("K", [256, 7168])
-def test_gemm_bf16_row_scale_bit_exact(K):
+@pytest.mark.parametrize("K,n_out,tile_rows", [(256, 384, None), (7168, 384, None),
+                                               (256, 512, 256), (2048, 512, 256)])
+def test_gemm_bf16_row_scale_bit_exact(K, n_out, tile_rows):
     """The bf16 epilogue's per-row multiplier: out = bf16(fl32(C * row_scale))
     with C exact (integer operands, power-of-two scales), so the result is
-    bit-exact: the float32 product, then round to nearest even bf16.  K = 256
-    runs the single-group K loop, K = 7168 the ping-pong."""
+    bit-exact: the float32 product, then round to nearest even bf16.  With
+    128-row tiles K = 256 runs the single-group K loop, K = 7168 the
+    ping-pong; the others run the 256-row kernel."""
     moe = _moe()
     rng = np.random.default_rng(K + 5)
     sizes = [70, 0, 200, 1]
     off = _ragged_offsets(sizes)
-    R, G, n_out = int(off[-1]), len(sizes), 384
+    R, G = int(off[-1]), len(sizes)
     aq = _int_codes(rng, (R + 9, K))
     ad = np.full((R + 9, K // 128), 2.0 ** -3, np.float32)
     bq = _int_codes(rng, (G, n_out, K))
@@ -531,10 +538,10 @@ def test_gemm_bf16_row_scale_bit_exact(K):
         if rr.size:
             c[rr] = ffn.block_scaled_gemm(aq[rix[rr]], ad[rix[rr]], bq[g], bd[g])
     want = ffn.bf16_round((c.astype(np.float32) * rs[:, None]).astype(np.float64))
-    log(f"moe_grouped_gemm_fp8 bf16 row_scale K={K}")
+    log(f"moe_grouped_gemm_fp8 bf16 row_scale K={K} n_out={n_out} tile_rows={tile_rows}")
     out, _ = moe.moe_grouped_gemm_fp8(to_dev(aq), to_dev(ad), to_dev(bq), to_dev(bd),
                                       to_dev(off), R, moe.MOE_EPI_BF16, a_row_index=to_dev(rix),
-                                      row_scale=to_dev(rs))
+                                      row_scale=to_dev(rs), tile_rows=tile_rows)
     torch.cuda.synchronize()
     assert np.array_equal(out.float().cpu().numpy().astype(np.float64), want)
 
@@ -811,6 +818,34 @@ def test_gemm_swiglu_tile_sizes_agree_bit_exact(K):
         np.testing.assert_array_equal(got[t][0], got[128][0])
         np.testing.assert_array_equal(got[t][1].view(np.uint32), got[128][1].view(np.uint32))
     assert np.count_nonzero(got[128][0]) > R * I // 4      # the outputs carry data
+
+
+@pytest.mark.parametrize("K", [128, 384, 2048, 2176])
+def test_gemm_bf16_tile_sizes_agree_bit_exact(K):
+    """The 256-row and 128-row kernels with the bf16 epilogue: the same
+    per-block products and fused multiply-adds per output, so identical bf16
+    outputs, on random operands, ragged groups straddling both tile heights
+    and 1 to 17 K blocks (the 128-row kernel runs its single-group loop up to
+    16 K blocks and the ping-pong beyond)."""
+    moe = _moe()
+    rng = np.random.default_rng(2000 + K)
+    n_out = 768
+    sizes = [1, 0, 255, 256, 257, 300, 17, 511, 512, 513, 64, 65, 129, 0, 3]
+    off = _ragged_offsets(sizes)
+    R, G = int(off[-1]), len(sizes)
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((R, K)).astype(np.float32))
+    aq, ad = moe.fp8_quant_1x128(bf16_to_dev(xb))
+    w = synth.f32_to_bf16_bits((rng.standard_normal((G, n_out, K)) * 0.03).astype(np.float32))
+    bq, bd = moe.fp8_quant_128x128(bf16_to_dev(w))
+    got = {}
+    for t in (128, 256, 0):
+        log(f"moe_grouped_gemm_fp8_tiles bf16 K={K} tile_rows={t}")
+        out, _ = moe.moe_grouped_gemm_fp8(aq, ad, bq, bd, to_dev(off), R, moe.MOE_EPI_BF16, tile_rows=t)
+        torch.cuda.synchronize()
+        got[t] = out.view(torch.int16).cpu().numpy()
+    for t in (256, 0):
+        np.testing.assert_array_equal(got[t], got[128])
+    assert np.count_nonzero(got[128]) > R * n_out // 2
 
 
 def _gpu_silu_rel_bound(g):
