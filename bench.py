@@ -477,8 +477,8 @@ def bench_backward(args, w, moe, torch, gen, lay, st):
         roof = {"bound": "mfma", "achieved": round(fl / t_dom / 1e12, 2), "peak": FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(fl / t_dom / 1e12 / FP8_PEAK_TFLOPS, 4)}
     kname = {"wgrad1": "wgrad_kernel (dW1)", "wgrad2": "wgrad_kernel (dW2)",
-             "dgrad1": "grouped_gemm_kernel<0> (dX, Dgrad of W1)",
-             "dgrad2": "grouped_gemm_kernel<0> (dH, Dgrad of W2)"}[dom]
+             "dgrad1": "grouped_gemm256_kernel<BF16> (dX, Dgrad of W1)",
+             "dgrad2": "grouped_gemm256_kernel<BF16> (dH, Dgrad of W2)"}[dom]
     roof.update({"traffic": None, "kernel": kname, "kernel_avg_ms": round(kern[dom], 4),
                  "algorithmic_bytes_per_launch": by, "algorithmic_flops_per_launch": fl,
                  "mfma_tflops": round(fl / t_dom / 1e12, 2),
@@ -828,7 +828,7 @@ def main():
     r1 = roofline_of(g1_flops, g1_bytes, kern["gemm1"])
     roof = {k_: r1[k_] for k_ in ("bound", "achieved", "peak", "unit", "frac")}
     roof.update({"traffic": measured_traffic(args.workload),
-                 "kernel": "grouped_gemm256_swiglu_kernel (GEMM1, 256-row tiles)",
+                 "kernel": "grouped_gemm256_kernel<SWIGLU_FP8> (GEMM1, 256-row tiles)",
                  "kernel_avg_ms": round(kern["gemm1"], 4),
                  "algorithmic_bytes_per_launch": g1_bytes,
                  "algorithmic_flops_per_launch": g1_flops})

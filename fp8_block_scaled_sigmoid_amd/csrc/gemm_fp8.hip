@@ -77,7 +77,6 @@ constexpr int kStages = 3;
 constexpr int kSWin = 8;                                // K blocks per A-scale window
 constexpr int kSWinBytes = BM * kSWin * 4;              // 4 KiB: [128 rows][8 K blocks]
 constexpr int kSWinOff = kStages * kStage;              // A scales after the ring
-constexpr int kLds = kSWinOff + 2 * kSWinBytes;         // 152 KiB
 // The single-group K loop keeps one K block's 128 A scales at the end of each
 // of its stages instead: its reads are four 16-byte loads per K block, where
 // the window's [row][8] layout would take sixteen 4-byte ones.
