@@ -888,6 +888,7 @@ constexpr int kSWin256 = BM256 * kSWin * 4;             // 8 KiB
 constexpr int kSWinOff256 = 2 * kStage256;              // 128 KiB
 constexpr int kDummy256 = kSWinOff256 + 2 * kSWin256;   // takes the dropped window copies
 constexpr int kLds256 = kDummy256 + 8 * 1024;           // 152 KiB
+static_assert(256 * 264 * 2 <= kLds256, "the bf16 epilogue's staging tile fits");
 
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm256_kernel(GemmParams p) {
@@ -1154,10 +1155,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm256_kernel(GemmParams
   __syncthreads();   // every wave is done with the stages and windows (no copy is in flight)
 
   if constexpr (EPI == MOE_EPI_BF16) {
-    // ---- bf16 epilogue: staged through LDS ([256][256] bf16 over both stage
-    // slots), then 16 coalesced 16-byte buffer stores per thread; a row past
-    // the tile's valid rows points past the buffer's end, where the store is
-    // dropped.  Lane value (mi, ni, v) sits at tile row wm*64 + mi*16 + 4*lk + v
+    // ---- bf16 epilogue: staged through LDS ([256][264] bf16 over both stage
+    // slots and the windows; the 8 pad columns put the rows that four lane
+    // groups write together, 4 rows apart, on different banks), then 16
+    // coalesced 16-byte buffer stores per thread; a row past the tile's valid
+    // rows points past the buffer's end, where the store is dropped.  Lane value (mi, ni, v) sits at tile row wm*64 + mi*16 + 4*lk + v
     // and column wn*128 + ni*16 + lrow.
     uint16_t* otile = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
@@ -1170,7 +1172,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm256_kernel(GemmParams
 #pragma unroll
         for (int ni = 0; ni < 8; ++ni) {
           const float val = p.row_scale ? acc[mi][ni][v] * rs : acc[mi][ni][v];
-          otile[row * 256 + wn * 128 + ni * 16 + lrow] = (uint16_t)f32_to_bf16(val);
+          otile[row * 264 + wn * 128 + ni * 16 + lrow] = (uint16_t)f32_to_bf16(val);
         }
       }
     __syncthreads();
@@ -1182,7 +1184,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm256_kernel(GemmParams
       const int q = tid + kThreads * j;
       const int row = q >> 5, c = q & 31;
       const int off = row < rows_valid ? (row * (int)p.ldo + n_tile * BN + c * 8) * 2 : 0x7FFFFFF0;
-      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const i32x4*>(otile + row * 256 + c * 8), rs_o,
+      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const i32x4*>(otile + row * 264 + c * 8), rs_o,
                                              off, 0, 0);
     }
   } else {

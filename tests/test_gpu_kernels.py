@@ -588,13 +588,16 @@ def test_strided_rows_bit_exact():
 
 def test_gemm_many_groups_bit_exact():
     """1025 groups (the most the tile scan takes, three per thread), most of
-    them empty, the others of 1 to 140 rows, integer operands: bit-exact."""
+    them empty, the others of 1 to 140 rows and a few split over two or three
+    256-row tiles, integer operands: bit-exact with the float32 epilogue and
+    with the bf16 one on both row tiles."""
     moe = _moe()
     rng = np.random.default_rng(1025)
     G, K, n_out = 1025, 256, 256
     sizes = np.zeros(G, np.int64)
     live = rng.choice(G, 40, replace=False)
     sizes[live] = rng.integers(1, 141, live.size)
+    sizes[live[:3]] = [300, 513, 257]       # split over several 256-row tiles
     sizes[G - 1] = 129                      # the last group: a one-row tail
     off = _ragged_offsets(sizes)
     R = int(off[-1])
@@ -608,11 +611,13 @@ def test_gemm_many_groups_bit_exact():
     for g in np.nonzero(sizes)[0]:
         rr = np.arange(off[g], off[g + 1])
         want[rr] = ffn.block_scaled_gemm(aq[rr], ad[rr], bq[g], bd[g])
-    log("moe_grouped_gemm_fp8 1025 groups")
-    out, _ = moe.moe_grouped_gemm_fp8(to_dev(aq), to_dev(ad), to_dev(bq), to_dev(bd),
-                                      to_dev(off), R, moe.MOE_EPI_F32)
-    torch.cuda.synchronize()
-    assert np.array_equal(out.cpu().numpy().astype(np.float64), want)
+    for epi, tile_rows in ((moe.MOE_EPI_F32, None), (moe.MOE_EPI_BF16, 128), (moe.MOE_EPI_BF16, 256)):
+        log(f"moe_grouped_gemm_fp8 1025 groups epi={epi} tile_rows={tile_rows}")
+        out, _ = moe.moe_grouped_gemm_fp8(to_dev(aq), to_dev(ad), to_dev(bq), to_dev(bd),
+                                          to_dev(off), R, epi, tile_rows=tile_rows)
+        torch.cuda.synchronize()
+        ref = want if epi == moe.MOE_EPI_F32 else ffn.bf16_round(want)
+        assert np.array_equal(out.float().cpu().numpy().astype(np.float64), ref)
 
 
 @pytest.mark.parametrize("n_out,K", [(6912, 128), (7040, 128), (7040, 384)])
