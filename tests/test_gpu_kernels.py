@@ -586,6 +586,56 @@ def test_strided_rows_bit_exact():
     assert not got[:, :64].any() and not got[:, 64 + n_out:].any()   # nothing outside the slice
 
 
+def test_strided_rows_256_row_tiles():
+    """The 256-row kernel with row strides larger than the row: A read as a
+    column slice (lda > K), the bf16 output written into a column slice of a
+    wider array (ldo > n_out, bit-exact against the oracle), and the SwiGLU
+    codes into a column slice of a wider byte array (identical to the
+    128-row kernel's); nothing outside either slice is written."""
+    moe = _moe()
+    rng = np.random.default_rng(78)
+    K, n_out = 384, 512
+    sizes = [300, 3, 0, 257]
+    off = _ragged_offsets(sizes)
+    R, G = int(off[-1]), len(sizes)
+    a_wide = _int_codes(rng, (R, K + 256))
+    aq = a_wide[:, 128:128 + K]
+    ad = np.full((R, K // 128), 2.0 ** -3, np.float32)
+    bq = _int_codes(rng, (G, n_out, K))
+    bd = np.full((G, n_out // 128, K // 128), 2.0 ** -5, np.float32)
+    want = np.zeros((R, n_out))
+    for g in range(G):
+        rr = np.arange(off[g], off[g + 1])
+        if rr.size:
+            want[rr] = ffn.block_scaled_gemm(aq[rr], ad[rr], bq[g], bd[g])
+    out_wide = torch.zeros(R, n_out + 128, dtype=torch.bfloat16, device="cuda")
+    log("moe_grouped_gemm_fp8_tiles bf16 strided A and output, 256-row tiles")
+    moe.moe_grouped_gemm_fp8(to_dev(a_wide)[:, 128:128 + K], to_dev(ad), to_dev(bq), to_dev(bd),
+                             to_dev(off), R, moe.MOE_EPI_BF16, out=out_wide[:, 64:64 + n_out], tile_rows=256)
+    torch.cuda.synchronize()
+    got = out_wide.float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(got[:, 64:64 + n_out], ffn.bf16_round(want))
+    assert not got[:, :64].any() and not got[:, 64 + n_out:].any()
+    # SwiGLU codes into a slice of a wider byte array, on both row tiles
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((R, K)).astype(np.float32))
+    xq, xd = moe.fp8_quant_1x128(bf16_to_dev(xb))
+    w1 = synth.f32_to_bf16_bits((rng.standard_normal((G, n_out, K)) * 0.05).astype(np.float32))
+    w1q, w1d = moe.fp8_quant_128x128(bf16_to_dev(w1), interleave_gate_up=True)
+    got_h = {}
+    for t in (128, 256):
+        hq_wide = torch.zeros(R, n_out // 2 + 64, dtype=torch.uint8, device="cuda")
+        hd = torch.zeros(R, n_out // 256, dtype=torch.float32, device="cuda")
+        log(f"moe_grouped_gemm_fp8_tiles swiglu strided output tile_rows={t}")
+        moe.moe_grouped_gemm_fp8(xq, xd, w1q, w1d, to_dev(off), R, moe.MOE_EPI_SWIGLU_FP8,
+                                 out=hq_wide[:, 32:32 + n_out // 2], out_d=hd, tile_rows=t)
+        torch.cuda.synchronize()
+        got_h[t] = (hq_wide.cpu().numpy(), hd.cpu().numpy())
+    np.testing.assert_array_equal(got_h[256][0], got_h[128][0])
+    np.testing.assert_array_equal(got_h[256][1].view(np.uint32), got_h[128][1].view(np.uint32))
+    assert not got_h[256][0][:, :32].any() and not got_h[256][0][:, 32 + n_out // 2:].any()
+    assert np.count_nonzero(got_h[256][0][:, 32:32 + n_out // 2]) > R * n_out // 8
+
+
 def test_gemm_many_groups_bit_exact():
     """1025 groups (the most the tile scan takes, three per thread), most of
     them empty, the others of 1 to 140 rows and a few split over two or three
