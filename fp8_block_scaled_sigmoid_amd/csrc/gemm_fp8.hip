@@ -13,7 +13,13 @@
 // folded into the float running sum with one fused multiply-add by
 // d_A[row, kb] * d_B[col block, kb].
 //
-// Layout and schedule:
+// Two kernels compute it, with the same per-output arithmetic (so the same
+// results bit for bit): grouped_gemm256_kernel (256 x 256 tiles, below the
+// 128-row kernel) for the SwiGLU and bf16 epilogues when the groups hold at
+// least 128 rows on average, and grouped_gemm_kernel (128 x 256 tiles) for
+// small groups and the float32 epilogue.
+//
+// Layout and schedule of the 128-row kernel:
 //   * a workgroup of 8 waves (two per SIMD, so one wave's LDS reads overlap
 //     the other's MFMAs) computes a 128 x 256 output tile of one group
 //     (expert); wave (wm, wn) owns 64 rows x 64 columns = 4 x 4 MFMA subtiles,
