@@ -860,10 +860,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 }
 
 // ---- 256-row tiles for the SwiGLU and bf16 epilogues -----------------------
-// A workgroup of 8 waves computes a 256 x 256 tile (256 rows of one group,
-// one interleaved gate/up block pair); wave (wm, wn) owns rows wm*64..+64 and
-// the 128 columns of weight block wn (0 gate, 1 up): 4 x 8 MFMA subtiles, 128
-// float accumulators.  Per 8.4 MFLOP it moves 16 KiB of A and 16 KiB of B
+// A workgroup of 8 waves computes a 256 x 256 tile: up to 256 rows of one
+// group (its rows split evenly over its row tiles) by two 128-column weight
+// blocks (with the SwiGLU epilogue the interleaved gate/up pair); wave
+// (wm, wn) owns rows wm*64..+64 and the 128 columns of weight block wn: 4 x 8
+// MFMA subtiles, 128 float accumulators.  Per 8.4 MFLOP it moves 16 KiB of A and 16 KiB of B
 // through the compute unit's L1 instead of the 128-row tile's 16 + 32 KiB:
 // each weight line is read once per 256 rows, not twice.
 //   * LDS: two 64 KiB stages (A 256 x 128 B, B 256 x 128 B, rows laid out as
@@ -884,9 +885,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 //   * Inside a column subtile each MFMA is followed by the 4 scale FMAs of the
 //     previous subtile's same row subtile, so the VALU works while the wave's
 //     own MFMAs run (the partials are double-buffered).
-//   * The gate and up waves of a row band are adjacent (wm = (w >> 1) & 3,
-//     wn = w & 1), so they run on different SIMDs (wave w runs on SIMD w % 4)
-//     and a tile with few live rows still uses two SIMDs per band.
+//   * The two waves of a row band are adjacent (wm = (w >> 1) & 3, wn = w & 1),
+//     so they run on different SIMDs (wave w runs on SIMD w % 4) and a tile
+//     with few live rows still uses two SIMDs per band.
+//   * Epilogues: SwiGLU + 1x128 requantisation (the gate and up waves of a
+//     band swap half their columns through LDS) or bf16 (staged through LDS);
+//     both write with coalesced 16-byte stores.
 constexpr int BM256 = 256;
 constexpr int kA256 = BM256 * BK;                       // 32 KiB
 constexpr int kStage256 = kA256 + kBBytes;              // 64 KiB
