@@ -690,7 +690,7 @@ def sub_workload(name, args, moe, torch, st, dev, wq):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the layer runs on one GPU; --gpus {args.gpus} is not supported "
               "(the expert-parallel design across GPUs is described, not built)", file=sys.stderr)
         sys.exit(2)
     import torch
