@@ -14,8 +14,8 @@
 // direct-to-LDS copies three stages deep, and writes them to the workspace.
 // The second launch takes one wave per token: it sums the S partial logits in
 // slice order (so the result does not depend on timing), applies the
-// sigmoid, and selects the top k by k rounds of a wave-wide argmax on a
-// (key, -index) composite, which gives ties to the lower index.
+// sigmoid, and selects the top k by k rounds of a wave-wide maximum of the
+// keys as order-preserving integers, a ballot giving ties to the lower index.
 #include <type_traits>
 
 #include "common.h"
@@ -74,44 +74,81 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
   return best;
 }
 
-// k rounds of wave-wide argmax over keys held PER lane-slots per lane (expert
-// e = lane + 64 * slot).  On return lane j < k holds the j-th chosen expert in
-// sel_idx and its unbiased score in sel_s; `sum` (wave-uniform) is the float
-// sum of the chosen scores in selection order.
+// Wave-wide maximum of a 32-bit unsigned value (uniform result): the row
+// maxima by the same four DPP steps, then row 0's maximum broadcast into row
+// 1 and row 2's into row 3, then row 1's into rows 2 and 3, so that lane 63
+// holds the maximum of the wave.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  uint32_t o;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+  v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+  v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);
+  v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false);
+  v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);   // row_bcast:31
+  v = o > v ? o : v;
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// k rounds of wave-wide argmax over keys held PER slots per lane, expert
+// e = lane * PER + slot (each lane holds PER consecutive experts).  On return
+// lane j < k holds the j-th chosen expert in sel_idx and its unbiased score in
+// sel_s; `sum` (wave-uniform) is the float sum of the chosen scores in
+// selection order.
+//
+// Each slot holds its key as an order-preserving 32-bit integer (at least 1;
+// 0 marks a slot that is taken, excluded or beyond N).  A round takes the
+// wave maximum m; the lowest lane whose own maximum equals m (a ballot) holds
+// the lowest expert index with key m, at its lowest slot equal to m, so ties
+// go to the lower index as in a (key, -index) argmax.  Equal integers are
+// equal keys, except that the two most negative NaN patterns share the value
+// 1.  The rounds run on the vector unit but for the ballot and two reads of
+// one lane.
 template <int PER>
 __device__ __forceinline__ void wave_topk(const float (&key)[PER], const float (&score)[PER],
                                           int N, int k, int lane, int& sel_idx, float& sel_s,
                                           float& sum, uint32_t excluded = 0u) {
-  uint32_t taken = excluded;
-  sum = 0.0f;
-  sel_idx = -1;
-  sel_s = 0.0f;
-  for (int r = 0; r < k; ++r) {
-    unsigned long long best = 0ull;
+  uint32_t cand[PER];
 #pragma unroll
-    for (int s = 0; s < PER; ++s) {
-      const int e = lane + 64 * s;
-      if (e < N && !((taken >> s) & 1u)) {
-        const unsigned long long c =
-            ((unsigned long long)sortable(key[s]) << 32) | (0xFFFFFFFFu - (uint32_t)e);
-        best = c > best ? c : best;
-      }
-    }
-    best = wave_max_u64(best);
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
-    const int owner = e & 63, slot = e >> 6;
-    float s_e = 0.0f;
-#pragma unroll
-    for (int s = 0; s < PER; ++s)
-      if (s == slot) s_e = score[s];
-    s_e = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_e), owner));
-    if (lane == owner) taken |= 1u << slot;
-    sum = sum + s_e;
-    if (lane == r) {
-      sel_idx = e;
-      sel_s = s_e;
-    }
+  for (int s = 0; s < PER; ++s) {
+    const uint32_t u = sortable(key[s]);
+    cand[s] = (lane * PER + s < N && !((excluded >> s) & 1u)) ? (u > 1u ? u : 1u) : 0u;
   }
+  sel_idx = -1;
+  for (int r = 0; r < k; ++r) {
+    uint32_t best = cand[0];
+#pragma unroll
+    for (int s = 1; s < PER; ++s) best = cand[s] > best ? cand[s] : best;
+    const uint32_t m = wave_max_u32(best);
+    // k never exceeds the eligible experts, so some lane's maximum equals m
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(best == m);
+    const int owner = (int)__builtin_ctzll(hit | (1ull << 63));
+    int first = PER - 1;
+#pragma unroll
+    for (int s = PER - 2; s >= 0; --s) first = cand[s] == m ? s : first;
+    const int e = owner * PER + __builtin_amdgcn_readlane(first, owner);
+#pragma unroll
+    for (int s = 0; s < PER; ++s) cand[s] = lane * PER + s == e ? 0u : cand[s];
+    if (lane == r) sel_idx = e;
+  }
+  // lane j < k fetches its expert's score from the lane that holds it
+  const int src = sel_idx < 0 ? lane : sel_idx / PER;
+  const int slot = sel_idx < 0 ? 0 : sel_idx % PER;
+  float got = 0.0f;
+#pragma unroll
+  for (int s = 0; s < PER; ++s) {
+    const float v = __shfl(score[s], src, 64);
+    got = slot == s ? v : got;
+  }
+  sel_s = sel_idx < 0 ? 0.0f : got;
+  sum = 0.0f;
+  for (int r = 0; r < k; ++r)
+    sum = sum + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel_s), r));
 }
 
 __device__ __forceinline__ float unsortable(uint32_t v) {
@@ -123,7 +160,7 @@ __device__ __forceinline__ float unsortable(uint32_t v) {
 // experts form G groups of N / G consecutive indices; a group's score is the
 // float sum of its r largest keys, added in descending order; only the M best
 // groups (score descending, group index ascending) are eligible.  Returns the
-// slots of this lane (expert lane + 64 p) that are NOT eligible, as a bit
+// slots of this lane (expert lane * PER + p) that are NOT eligible, as a bit
 // mask.  Requires G <= 64.
 template <int PER>
 __device__ __forceinline__ uint32_t group_excluded(const float (&key)[PER], int N, int G, int M,
@@ -137,7 +174,7 @@ __device__ __forceinline__ uint32_t group_excluded(const float (&key)[PER], int 
       unsigned long long best = 0ull;
 #pragma unroll
       for (int p = 0; p < PER; ++p) {
-        const int e = lane + 64 * p;
+        const int e = lane * PER + p;
         if (e < N && e / gs == g && !((taken >> p) & 1u)) {
           const unsigned long long c =
               ((unsigned long long)sortable(key[p]) << 32) | (0xFFFFFFFFu - (uint32_t)e);
@@ -146,7 +183,7 @@ __device__ __forceinline__ uint32_t group_excluded(const float (&key)[PER], int 
       }
       best = wave_max_u64(best);
       const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
-      if (lane == (e & 63)) taken |= 1u << (e >> 6);
+      if (lane == e / PER) taken |= 1u << (e % PER);
       const float kv = unsortable((uint32_t)(best >> 32));
       acc = j == 0 ? kv : acc + kv;
     }
@@ -161,7 +198,7 @@ __device__ __forceinline__ uint32_t group_excluded(const float (&key)[PER], int 
   uint32_t excluded = 0;
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
-    const int e = lane + 64 * p;
+    const int e = lane * PER + p;
     const int g = e < N ? e / gs : 0;
     const int ok = __shfl(chosen, g, 64);
     if (e >= N || !ok) excluded |= 1u << p;
@@ -457,8 +494,10 @@ __global__ __launch_bounds__(kRThreads, 1) void route_partial_fp8_kernel(
   }
 }
 
-// One wave per token: logits = sum of the S partials in slice order, scores =
-// sigmoid, then the biased top k and the unbiased gates.
+// One wave per token, each lane holding PER consecutive experts: logits = sum
+// of the S partials in slice order, scores = sigmoid, then the biased top k
+// and the unbiased gates.  A lane's PER partials, biases and scores are
+// adjacent, so each is one wide access.
 template <int PER>
 __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restrict__ ws, int S,
                                                            const float* __restrict__ bias, int T,
@@ -469,18 +508,29 @@ __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restri
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  const int e0 = lane * PER;
   float key[PER], scr[PER];
+  // N is a multiple of 16, so a lane holds all PER of its experts or none
+  if (e0 < N) {
+    float z[PER];
 #pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    const int e = lane + 64 * p;
-    float z = 0.0f;
-    if (e < N) {
-      z = ws[(long long)t * N + e];
-      for (int s = 1; s < S; ++s) z += ws[((long long)s * T + t) * N + e];
+    for (int p = 0; p < PER; ++p) z[p] = ws[(long long)t * N + e0 + p];
+    for (int s = 1; s < S; ++s) {
+#pragma unroll
+      for (int p = 0; p < PER; ++p) z[p] += ws[((long long)s * T + t) * N + e0 + p];
     }
-    scr[p] = e < N ? sigmoidf_acc(z) : 0.0f;
-    key[p] = e < N ? scr[p] + bias[e] : 0.0f;
-    if (scores && e < N) scores[(long long)t * N + e] = scr[p];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      scr[p] = sigmoidf_acc(z[p]);
+      key[p] = scr[p] + bias[e0 + p];
+    }
+    if (scores) {
+#pragma unroll
+      for (int p = 0; p < PER; ++p) scores[(long long)t * N + e0 + p] = scr[p];
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) scr[p] = key[p] = 0.0f;
   }
   const uint32_t excluded = G > 1 ? group_excluded<PER>(key, N, G, M, k / M, lane) : 0u;
   int sel;
@@ -492,7 +542,8 @@ __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restri
   }
 }
 
-// One wave per token over a given score tensor (N <= 64 * PER).
+// One wave per token over a given score tensor (N <= 64 * PER), each lane
+// holding PER consecutive experts.
 template <int PER>
 __global__ __launch_bounds__(256) void topk_scores_kernel(const float* __restrict__ scores,
                                                           const float* __restrict__ bias, int T,
@@ -505,7 +556,7 @@ __global__ __launch_bounds__(256) void topk_scores_kernel(const float* __restric
   float key[PER], scr[PER];
 #pragma unroll
   for (int s = 0; s < PER; ++s) {
-    const int e = lane + 64 * s;
+    const int e = lane * PER + s;
     scr[s] = e < N ? scores[(long long)t * N + e] : 0.0f;
     key[s] = e < N ? scr[s] + bias[e] : 0.0f;
   }
@@ -525,6 +576,20 @@ bool groups_ok(int N, int k, int G, int M) {
   if (G <= 1) return true;
   if (G > 64 || N % G != 0 || M < 1 || M > G || k % M != 0) return false;
   return k / M <= N / G && k <= M * (N / G);
+}
+
+// The finish launch shared by both routers: PER = ceil(N / 64) slots per lane.
+void launch_finish(const float* part, int S, const float* bias, int T, int N, int k, int G, int M,
+                   float* scores, int32_t* idx, float* gate, hipStream_t stream) {
+  const int blocks = (T + 3) / 4;
+  const int per = (N + 63) / 64;
+#define MOE_FINISH_LAUNCH(P)                                                                  \
+  hipLaunchKernelGGL(route_finish_kernel<P>, dim3(blocks), dim3(256), 0, stream, part, S, bias, \
+                     T, N, k, G, M, scores, idx, gate)
+  if (per <= 1) MOE_FINISH_LAUNCH(1);
+  else if (per <= 2) MOE_FINISH_LAUNCH(2);
+  else MOE_FINISH_LAUNCH(4);
+#undef MOE_FINISH_LAUNCH
 }
 
 }  // namespace
@@ -562,15 +627,8 @@ extern "C" moe_status_t moe_route_topk(const void* x_bf16, const void* w_router_
                      static_cast<const uint16_t*>(x_bf16),
                      static_cast<const uint16_t*>(w_router_bf16), T, H, N, S, part);
   if (moe_status_t st = launch_status()) return st;
-  const int blocks = (T + 3) / 4;
-  const int per = (N + 63) / 64;
-#define MOE_FINISH_LAUNCH(P)                                                                  \
-  hipLaunchKernelGGL(route_finish_kernel<P>, dim3(blocks), dim3(256), 0, stream, part, S, bias, \
-                     T, N, k, n_groups, topk_groups, scores, topk_idx, topk_gate)
-  if (per <= 1) MOE_FINISH_LAUNCH(1);
-  else if (per <= 2) MOE_FINISH_LAUNCH(2);
-  else MOE_FINISH_LAUNCH(4);
-#undef MOE_FINISH_LAUNCH
+  launch_finish(part, S, bias, T, N, k, n_groups, topk_groups, scores, topk_idx, topk_gate,
+                stream);
   return launch_status();
 }
 
@@ -606,15 +664,8 @@ extern "C" moe_status_t moe_route_topk_fp8(const uint8_t* x_q, const float* x_d,
   hipLaunchKernelGGL(route_partial_fp8_kernel, dim3(grid), dim3(kRThreads), kRLdsF, stream, x_q,
                      x_d, w_router_q, w_router_d, T, H, N, S, part);
   if (moe_status_t st = launch_status()) return st;
-  const int blocks = (T + 3) / 4;
-  const int per = (N + 63) / 64;
-#define MOE_FINISH_LAUNCH(P)                                                                  \
-  hipLaunchKernelGGL(route_finish_kernel<P>, dim3(blocks), dim3(256), 0, stream, part, S, bias, \
-                     T, N, k, n_groups, topk_groups, scores, topk_idx, topk_gate)
-  if (per <= 1) MOE_FINISH_LAUNCH(1);
-  else if (per <= 2) MOE_FINISH_LAUNCH(2);
-  else MOE_FINISH_LAUNCH(4);
-#undef MOE_FINISH_LAUNCH
+  launch_finish(part, S, bias, T, N, k, n_groups, topk_groups, scores, topk_idx, topk_gate,
+                stream);
   return launch_status();
 }
 
