@@ -164,6 +164,28 @@ def test_quant_1x128_f32_random_tiles():
     assert np.array_equal(q.cpu().numpy(), wq) and np.array_equal(d.cpu().numpy(), wd)
 
 
+@pytest.mark.parametrize("tiles", [1, 3, 4, 5, 7, 9])
+def test_quant_1x128_runs_and_row_stride(tiles):
+    """Rows of 1-9 tiles (the quantiser takes runs of four tiles of a row, so
+    every remainder of a run occurs) read from a wider tensor (row stride
+    larger than the row), 37 rows."""
+    moe = _moe()
+    rng = np.random.default_rng(40 + tiles)
+    cols = 128 * tiles
+    full = (rng.standard_normal((37, cols + 136)) *
+            np.exp(rng.uniform(-8, 8, (37, 1)))).astype(np.float32)
+    full[5, :] = 0.0                                       # zero tiles
+    full[9, 128 * (tiles - 1) + 3] = 3e4                   # outlier in the last tile
+    bits = synth.f32_to_bf16_bits(full)
+    x = bf16_to_dev(bits)[:, 8:8 + cols]                   # stride cols + 136, offset 16 bytes
+    log(f"fp8_quant_1x128 bf16 tiles={tiles} ld={x.stride(0)}")
+    q, d = moe.fp8_quant_1x128(x)
+    torch.cuda.synchronize()
+    wq, wd = quant.quant_1x128(synth.as_f64(bits[:, 8:8 + cols]))
+    assert np.array_equal(q.cpu().numpy(), wq)
+    assert np.array_equal(d.cpu().numpy(), wd)
+
+
 @pytest.mark.parametrize("interleave", [False, True])
 def test_quant_128x128_bit_exact(interleave):
     moe = _moe()
