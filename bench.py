@@ -552,13 +552,12 @@ def cpu_baseline_backward(w, R):
 
 def layer_step_fns(lay, xs, cur, router_fp8):
     """The launches of one layer step, in order, with their names."""
-    names = ["route", "permute", "quant_x", "gemm1", "gemm2", "combine", "bias"]
-    fns = [lambda: lay.route(xs[cur["i"] % len(xs)]), lay.permute,
-           lambda: lay.quant_x(xs[cur["i"] % len(xs)]), lay.gemm1, lay.gemm2,
+    names = ["route", "permute", "gemm1", "gemm2", "combine", "bias"]
+    fns = [lambda: lay.route(xs[cur["i"] % len(xs)]), lay.permute, lay.gemm1, lay.gemm2,
            lay.combine, lay.bias_update]
     if router_fp8:    # the FP8 router reads the quantised x: quantise first
-        names = ["quant_x"] + names[:2] + names[3:]
-        fns = [fns[2]] + fns[:2] + fns[3:]
+        names = ["quant_x"] + names
+        fns = [lambda: lay.quant_x(xs[cur["i"] % len(xs)])] + fns
     return names, fns
 
 
@@ -598,13 +597,17 @@ def time_layer_steps(torch, st, names, fns, cur, steps, warmup):
     return ms_step, kern, step_ms, wall, step
 
 
-def gemm_work(w):
+def gemm_work(w, counts=None):
     """FLOPs of both expert GEMMs, and the algorithmic HBM bytes of one GEMM1
     launch (every W1 code and scale once, every token's x codes and scales
     once, the row map, the h codes and scales out) and of one GEMM2 launch
     (every W2 code and scale once, the h codes and scales, the expert rows
-    out)."""
+    out).  With the routed experts' row counts given, only the weights of the
+    groups that hold rows count (the GEMMs never read the others); the shared
+    expert always holds T rows."""
     R, G, T, H, I = w.R, w.G, w.T, w.H, w.I
+    if counts is not None:
+        G = int(np.count_nonzero(np.asarray(counts) > 0)) + 1
     g1_flops = 2.0 * R * H * 2 * I
     g2_flops = 2.0 * R * I * H
     g1_bytes = (G * 2 * I * H + G * (2 * I // 128) * (H // 128) * 4
@@ -657,12 +660,13 @@ def sub_workload(name, args, moe, torch, st, dev, wq):
         lay.forward(x)
         c = lay.counts.cpu().numpy()
         loads.append(round(float(c.max() / c.mean()), 3))
+        used = int(np.count_nonzero(c > 0))
     bias.copy_(b0)
     cur = {"i": 0}
     names, fns = layer_step_fns(lay, xs, cur, False)
     ms_step, kern, step_ms, _, _ = time_layer_steps(torch, st, names, fns, cur, args.steps,
                                                     args.warmup)
-    g1f, g2f, g1b, g2b = gemm_work(w)
+    g1f, g2f, g1b, g2b = gemm_work(w, c)
     tf = (g1f + g2f) / ((kern["gemm1"] + kern["gemm2"]) * 1e-3) / 1e12
     res = {"config": f"{w.name}: T={w.T} tokens, hidden {w.H}, {w.N} routed experts top-{w.k} "
                      f"+ 1 shared, SwiGLU intermediate {w.I}"
@@ -681,6 +685,7 @@ def sub_workload(name, args, moe, torch, st, dev, wq):
                                   kernel_avg_ms=round(kern["gemm2"], 4),
                                   algorithmic_bytes_per_launch=g2b),
            "kernel_ms": {n: round(v, 4) for n, v in kern.items()},
+           "routed_experts_with_rows": used,
            "expert_load_max_over_mean": loads if w.batches > 1 else loads[0]}
     del lay, xs, weights
     torch.cuda.empty_cache()
@@ -761,7 +766,7 @@ def main():
     # in the caches (combine reads the expert outputs GEMM2 has just written),
     # which would overstate its HBM rate
     cold = {}
-    for n in ("route", "permute", "quant_x", "combine"):
+    for n in [n_ for n_ in ("route", "permute", "quant_x", "combine") if n_ in names]:
         f = fns[names.index(n)]
         cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
@@ -822,7 +827,7 @@ def main():
         load_ratio.append(round(float(c.max() / c.mean()), 3))
 
     R, G, T, H, I = w.R, w.G, w.T, w.H, w.I
-    g1_flops, g2_flops, g1_bytes, g2_bytes = gemm_work(w)
+    g1_flops, g2_flops, g1_bytes, g2_bytes = gemm_work(w, c)
     gemm_tflops = (g1_flops + g2_flops) / ((kern["gemm1"] + kern["gemm2"]) * 1e-3) / 1e12
     tokens_per_s = w.T / (ms_step * 1e-3)
     r1 = roofline_of(g1_flops, g1_bytes, kern["gemm1"])
@@ -838,14 +843,17 @@ def main():
     # written once) over the measured kernel time
     N, k = w.N, w.k
     # (read, written) algorithmic bytes of each HBM phase
+    # (the bf16 router also writes the 1x128 codes and scales of x)
     phase_rw = {
         "route": ((N * H + (N // 128) * (H // 128) * 4 + T * H + T * (H // 128) * 4 + N * 4,
                    T * N * 4 + T * k * 8) if args.router_fp8 else
-                  (T * H * 2 + N * H * 2 + N * 4, T * N * 4 + T * k * 8)),
-        "quant_x": (T * H * 2, T * H + T * (H // 128) * 4),
+                  (T * H * 2 + N * H * 2 + N * 4,
+                   T * N * 4 + T * k * 8 + T * H + T * (H // 128) * 4)),
         "combine": (R * H * 2 + T * k * 8, T * H * 2),
         "permute": (T * k * 4, N * 4 + (N + 2) * 4 + T * k * 4 + R * 4),
     }
+    if args.router_fp8:
+        phase_rw["quant_x"] = (T * H * 2, T * H + T * (H // 128) * 4)
     peaks = measured_peaks(moe, torch, st)
     phases = {}
     for n, (rb, wb) in phase_rw.items():
@@ -892,6 +900,7 @@ def main():
         "kernel_ms": {n: round(v, 4) for n, v in kern.items()},
         "hbm_phases": phases,
         "expert_load_max_over_mean": load_ratio if w.batches > 1 else load_ratio[-1],
+        "routed_experts_with_rows": int(np.count_nonzero(c > 0)),
         "weight_quant_ms": round(t_wq1 + t_wq2, 3),
         "wall_s_timed": round(wall, 3),
     }

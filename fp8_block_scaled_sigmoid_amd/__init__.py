@@ -72,6 +72,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         sig = {
             "moe_route_topk": [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, ctypes.c_size_t, _P],
+            "moe_route_topk_quant_x": [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
+                                       ctypes.c_size_t, _P],
             "moe_route_topk_fp8": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P,
                                    ctypes.c_size_t, _P],
             "moe_topk_from_scores": [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P],
@@ -165,6 +167,35 @@ def moe_route_topk(x, w_router, bias, k, scores=True, idx=None, gate=None, ws=No
                                                   n_groups, topk_groups, _ptr(scores), _ptr(idx),
                                                   _ptr(gate), _ptr(ws), ws.numel(), _stream(stream)))
     return idx, gate, scores
+
+
+def moe_route_topk_quant_x(x, w_router, bias, k, x_q=None, x_d=None, scores=True, idx=None,
+                           gate=None, ws=None, n_groups=1, topk_groups=1, stream=None):
+    """moe_route_topk that also writes the 1x128 FP8 quantisation of x (the
+    codes and scales fp8_quant_1x128 gives) from the same read of x.
+    Returns (idx, gate, scores, x_q uint8 [T,H], x_d float32 [T,H/128])."""
+    T, H = x.shape
+    N = w_router.shape[0]
+    _dev(x, torch.bfloat16, "x"), _dev(w_router, torch.bfloat16, "w_router")
+    _dev(bias, torch.float32, "bias")
+    if scores is True:
+        scores = torch.empty(T, N, dtype=torch.float32, device=x.device)
+    elif scores is False:
+        scores = None
+    idx = torch.empty(T, k, dtype=torch.int32, device=x.device) if idx is None else idx
+    gate = torch.empty(T, k, dtype=torch.float32, device=x.device) if gate is None else gate
+    x_q = torch.empty(T, H, dtype=torch.uint8, device=x.device) if x_q is None else x_q
+    x_d = torch.empty(T, H // 128, dtype=torch.float32, device=x.device) if x_d is None else x_d
+    _dev(x_q, torch.uint8, "x_q"), _dev(x_d, torch.float32, "x_d")
+    if ws is None:
+        ws = torch.empty(max(moe_route_workspace_bytes(T, H, N), 16), dtype=torch.uint8,
+                         device=x.device)
+    _check("moe_route_topk_quant_x",
+           lib().moe_route_topk_quant_x(_ptr(x), _ptr(w_router), _ptr(bias), T, H, N, k, n_groups,
+                                        topk_groups, _ptr(scores), _ptr(idx), _ptr(gate),
+                                        _ptr(x_q), _ptr(x_d), _ptr(ws), ws.numel(),
+                                        _stream(stream)))
+    return idx, gate, scores, x_q, x_d
 
 
 def moe_route_topk_fp8(x_q, x_d, w_router_q, w_router_d, bias, k, scores=True, idx=None,
@@ -534,17 +565,20 @@ class MoELayer:
 
     # the individual steps, so that callers can time or replace one of them
     def route(self, x, stream=None):
-        """Routing from x (bf16 router), or from the quantised x already in
-        self.xq / self.xd (FP8 router: quant_x runs first)."""
+        """Routing from x with the bf16 router, which also writes the 1x128
+        quantisation of x into self.xq / self.xd from the same read of x; or,
+        with the FP8 router, from the quantised x already there (quant_x runs
+        first)."""
         if self.router_fp8:
             moe_route_topk_fp8(self.xq, self.xd, self.w.w_router_q, self.w.w_router_d,
                                self.w.bias, self.k, scores=self.scores, idx=self.idx,
                                gate=self.gate, ws=self.route_ws, n_groups=self.n_groups,
                                topk_groups=self.topk_groups, stream=stream)
             return
-        moe_route_topk(x, self.w.w_router, self.w.bias, self.k, scores=self.scores, idx=self.idx,
-                       gate=self.gate, ws=self.route_ws, n_groups=self.n_groups,
-                       topk_groups=self.topk_groups, stream=stream)
+        moe_route_topk_quant_x(x, self.w.w_router, self.w.bias, self.k, x_q=self.xq, x_d=self.xd,
+                               scores=self.scores, idx=self.idx, gate=self.gate,
+                               ws=self.route_ws, n_groups=self.n_groups,
+                               topk_groups=self.topk_groups, stream=stream)
 
     def permute(self, stream=None):
         moe_permute(self.idx, self.w.N, self.with_shared,
@@ -576,12 +610,8 @@ class MoELayer:
         is updated from this batch's counts at the end."""
         if self.router_fp8:
             self.quant_x(x, stream)
-            self.route(x, stream)
-            self.permute(stream)
-        else:
-            self.route(x, stream)
-            self.permute(stream)
-            self.quant_x(x, stream)
+        self.route(x, stream)
+        self.permute(stream)
         self.gemm1(stream)
         self.gemm2(stream)
         self.combine(stream)

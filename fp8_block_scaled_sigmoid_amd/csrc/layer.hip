@@ -3,8 +3,8 @@
 // The steps are the library's own entry points, enqueued in order on one
 // stream ("DeepSeek-V3: Auxiliary-Loss-Free MoE Load Balancing, ...", section
 // III flowchart and Figure 2; "DeepSeek-V3, explained.", recipe steps 4-7):
-// sigmoid router and biased top-k, counts and permutation, 1x128 activation
-// quantisation, the grouped FP8 GEMM with the SwiGLU + requantisation
+// sigmoid router and biased top-k (which also writes the 1x128 activation
+// quantisation), counts and permutation, the grouped FP8 GEMM with the SwiGLU + requantisation
 // epilogue, the grouped FP8 down projection, the gate-weighted combine and,
 // last, the sign-based bias update from this batch's counts.  Every
 // intermediate lives in one caller-provided workspace, carved here into
@@ -126,7 +126,7 @@ extern "C" moe_status_t moe_layer_forward(const moe_layer_args* args, void* ws, 
 
   moe_status_t st;
   // x is quantised first when the FP8 router reads the codes; otherwise the
-  // routing and the permutation go ahead of the (independent) quantisation
+  // bf16 router quantises the x tiles it reads on the way
   if (a.router_fp8) {
     if ((st = fp8_quant_1x128(a.x, MOE_BF16, T, H, H, xq, xd, stream))) return st;
     if ((st = moe_route_topk_fp8(xq, xd, a.w_router_q, a.w_router_d, a.bias, T, H, N, k,
@@ -134,14 +134,14 @@ extern "C" moe_status_t moe_layer_forward(const moe_layer_args* args, void* ws, 
                                  base + c.route_ws, c.route_ws_bytes, stream)))
       return st;
   } else {
-    if ((st = moe_route_topk(a.x, a.w_router, a.bias, T, H, N, k, a.n_groups, a.topk_groups,
-                             a.scores, idx, gate, base + c.route_ws, c.route_ws_bytes, stream)))
+    if ((st = moe_route_topk_quant_x(a.x, a.w_router, a.bias, T, H, N, k, a.n_groups,
+                                     a.topk_groups, a.scores, idx, gate, xq, xd,
+                                     base + c.route_ws, c.route_ws_bytes, stream)))
       return st;
   }
   if ((st = moe_permute(idx, T, N, k, a.with_shared ? 1 : 0, counts, offsets, row_of, token_of,
                         base + c.perm_ws, c.perm_ws_bytes, stream)))
     return st;
-  if (!a.router_fp8 && (st = fp8_quant_1x128(a.x, MOE_BF16, T, H, H, xq, xd, stream))) return st;
 
   moe_gemm_fp8_args g1{};
   g1.a_q = xq; g1.a_d = xd; g1.lda = H; g1.a_rows = T; g1.a_row_index = token_of;

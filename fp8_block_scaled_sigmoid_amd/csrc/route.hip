@@ -209,15 +209,17 @@ __device__ __forceinline__ uint32_t group_excluded(const float (&key)[PER], int 
 __device__ __forceinline__ float sigmoidf_acc(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 // Number of H slices for T tokens: enough workgroups for about one per
-// compute unit, at most one slice per 64-wide chunk, and at most 16 (the
-// partial logits, S * T * N floats written and read back, must stay small
-// next to x when T is small).
+// compute unit, at most one slice per 128-wide block of H (a slice holds
+// whole 1x128 tiles of x, which the quantising variant needs), and at most
+// 16 (the partial logits, S * T * N floats written and read back, must stay
+// small next to x when T is small).
 int route_splits(int T, int H) {
-  const int nc = H / kRKc;
+  const int nb = H / 128;
   const int tiles = (T + kRT - 1) / kRT;
   int S = (256 + tiles - 1) / tiles;
   if (S > 16) S = 16;
-  return S < 1 ? 1 : (S > nc ? nc : S);
+  if (S > nb) S = nb;
+  return S < 1 ? 1 : S;
 }
 
 __device__ __forceinline__ int clampi_dev(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
@@ -239,9 +241,22 @@ __device__ __forceinline__ void wait_and_barrier() {
 // Workgroup layout: the (slice, token tile) list is slice-major and each XCD
 // takes a contiguous run of it, so one XCD mostly reads one slice of Wr.
 // LDS rows are 128 B; 16-byte chunk c of row r sits at c ^ ((r >> 1) & 7).
+// A slice holds whole 128-wide blocks of H (two K chunks each).
+//
+// With QX the kernel also writes the 1x128 FP8 codes and scales of the x
+// tiles it holds (the activation quantisation of the expert GEMM, section V
+// of the same page, FP8 detail 1 and Figure 6), so x is read once for both:
+// the four threads of a token row each take 16 values of both K chunks of a
+// block (the first chunk's kept in registers until the second lands), the
+// block maximum is a 4-lane reduction, and the codes leave in two 16-byte
+// buffer stores per thread, the scale in one 4-byte store per row; rows past
+// T point past the buffers' ends, where the stores are dropped, so every wave
+// issues the same stores and the copy waits can count them.  The codes and
+// scales are those of fp8_quant_1x128 (the same scale rule and encoder).
+template <bool QX>
 __global__ __launch_bounds__(kRThreads, 1) void route_partial_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int H, int N, int S,
-    float* __restrict__ ws) {
+    float* __restrict__ ws, uint8_t* __restrict__ xq, float* __restrict__ xd) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -253,8 +268,8 @@ __global__ __launch_bounds__(kRThreads, 1) void route_partial_kernel(
   if (slot >= per_xcd || L >= total) return;
   const int s = L / tiles, tile = L - s * tiles;
   const int t0 = tile * kRT;
-  const int nc = H / kRKc;
-  const int c0 = (int)((long long)s * nc / S), c1 = (int)((long long)(s + 1) * nc / S);
+  const int nb = H / 128;
+  const int c0 = 2 * (int)((long long)s * nb / S), c1 = 2 * (int)((long long)(s + 1) * nb / S);
   const int nck = c1 - c0;
 
   // copies: load j of wave w fills the 1 KiB block 8 j + w of the stage
@@ -300,17 +315,99 @@ __global__ __launch_bounds__(kRThreads, 1) void route_partial_kernel(
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // quantiser: thread (row qr, part qp) holds x values 16 qp .. 16 qp + 15 of
+  // each K chunk of the row's current 128-wide block
+  const int qr = tid >> 2, qp = tid & 3;
+  const int qsw = (qr >> 1) & 7;
+  const int qpos0 = qr * 128 + (((2 * qp) ^ qsw) << 4);
+  const int qpos1 = qr * 128 + (((2 * qp + 1) ^ qsw) << 4);
+  const bool q_live = t0 + qr < T;
+  const int q_row = q_live ? (t0 + qr) * H : T * H;        // past the end: dropped
+  const int d_row = q_live ? (t0 + qr) * nb * 4 : T * nb * 4;
+  const __amdgpu_buffer_rsrc_t rs_q = make_rsrc(xq, QX ? T * H : 0);
+  const __amdgpu_buffer_rsrc_t rs_qd = make_rsrc(xd, QX ? T * nb * 4 : 0);
+  uint4 qv0 = make_uint4(0u, 0u, 0u, 0u), qv1 = qv0;      // first chunk's 16 bf16
+  float qmax = 0.0f;
+  i32x4 q_lo = i32x4{0, 0, 0, 0}, q_hi = q_lo;              // a finished block, not yet stored
+  float q_d = 1.0f;
+  // the first K chunk of a block (P = 0): keep its values, start the maximum;
+  // the second (P = 1): finish the maximum over the 4 threads of the row,
+  // form the scale and encode both chunks
+  auto quant_chunk = [&](auto p_c, const uint4& a, const uint4& b) {
+    constexpr int P = decltype(p_c)::value;
+    float v[16];
+    v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+    v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+    v[8] = bf16_lo(b.x); v[9] = bf16_hi(b.x); v[10] = bf16_lo(b.y); v[11] = bf16_hi(b.y);
+    v[12] = bf16_lo(b.z); v[13] = bf16_hi(b.z); v[14] = bf16_lo(b.w); v[15] = bf16_hi(b.w);
+    float m = P ? qmax : 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[e]));
+    if constexpr (P == 0) {
+      qv0 = a;
+      qv1 = b;
+      qmax = m;
+    } else {
+      m = group_max<4>(m);
+      float mul, dd;
+      tile_scale(m, mul, dd);
+      float u[16];
+      u[0] = bf16_lo(qv0.x); u[1] = bf16_hi(qv0.x); u[2] = bf16_lo(qv0.y);
+      u[3] = bf16_hi(qv0.y); u[4] = bf16_lo(qv0.z); u[5] = bf16_hi(qv0.z);
+      u[6] = bf16_lo(qv0.w); u[7] = bf16_hi(qv0.w); u[8] = bf16_lo(qv1.x);
+      u[9] = bf16_hi(qv1.x); u[10] = bf16_lo(qv1.y); u[11] = bf16_hi(qv1.y);
+      u[12] = bf16_lo(qv1.z); u[13] = bf16_hi(qv1.z); u[14] = bf16_lo(qv1.w);
+      u[15] = bf16_hi(qv1.w);
+      i32x4 c_lo, c_hi;
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) {
+        c_lo[w4] = (int)e4m3_pack4(u[4 * w4] * mul, u[4 * w4 + 1] * mul, u[4 * w4 + 2] * mul,
+                                   u[4 * w4 + 3] * mul);
+        c_hi[w4] = (int)e4m3_pack4(v[4 * w4] * mul, v[4 * w4 + 1] * mul, v[4 * w4 + 2] * mul,
+                                   v[4 * w4 + 3] * mul);
+      }
+      const bool zero = mul == 0.0f;        // the zero-tile rule: all codes +0
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) {
+        q_lo[w4] = zero ? 0 : c_lo[w4];
+        q_hi[w4] = zero ? 0 : c_hi[w4];
+      }
+      q_d = dd;
+    }
+  };
+  // the codes and scale of the block completed in K chunk i
+  auto quant_store = [&](int i) {
+    const int blk = (c0 + i) >> 1;
+    __builtin_amdgcn_raw_buffer_store_b128(q_lo, rs_q, q_row + blk * 128 + 16 * qp, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(q_hi, rs_q, q_row + blk * 128 + 64 + 16 * qp, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(q_d), rs_qd,
+                                          qp == 0 ? d_row + blk * 4 : T * nb * 4, 0, 0);
+  };
+
   auto kloop = [&](auto ni_c) {
     constexpr int NI = decltype(ni_c)::value;
     issue(0, smem);
     if (nck > 1) issue(1, smem + kRStage);
-    for (int i = 0; i < nck; ++i) {
+    // one K chunk; P is its position in its 128-wide block (nck is even, so
+    // chunk i has P = i & 1)
+    auto chunk = [&](int i, auto p_c) {
+      constexpr int P = decltype(p_c)::value;
+      // The quantiser's stores of the block finished in chunk i - 1 go out
+      // before the copies of chunk i + 2, so the next wait, which allows 6
+      // operations (those copies) to be outstanding, also covers them,
+      // whatever order loads and stores complete in.
       if (i + 1 < nck) wait_and_barrier<6>(); else wait_and_barrier<0>();
+      if (QX && P == 0 && i > 0) quant_store(i - 1);
       if (i + 2 < nck) issue(i + 2, smem + ((i + 2) % kRStages) * kRStage);
-      if (NI == 0) continue;
       const uint8_t* st = smem + (i % kRStages) * kRStage;
+      uint4 qa = make_uint4(0u, 0u, 0u, 0u), qb = qa;
+      if (QX) {
+        qa = *reinterpret_cast<const uint4*>(st + qpos0);
+        qb = *reinterpret_cast<const uint4*>(st + qpos1);
+      }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
+        if (NI == 0) break;
         const int fo = ks ? frag1 : frag0;
         bf16x8 af[4], bfr[NI > 0 ? NI : 1];
 #pragma unroll
@@ -325,7 +422,24 @@ __global__ __launch_bounds__(kRThreads, 1) void route_partial_kernel(
           for (int mi = 0; mi < 4; ++mi)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
       }
+      if (QX) {
+        quant_chunk(p_c, qa, qb);
+        // the quantiser's vector work between the MFMAs, so that it runs
+        // while they do
+        if (NI > 0) {
+#pragma unroll
+          for (int m = 0; m < 8 * NI; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, P ? 5 : 2, 0);
+          }
+        }
+      }
+    };
+    for (int i = 0; i < nck; i += 2) {
+      chunk(i, std::integral_constant<int, 0>{});
+      chunk(i + 1, std::integral_constant<int, 1>{});
     }
+    if (QX) quant_store(nck - 1);
     if (NI == 0) return;
     // lane value (mi, ni, v): token wm*64 + mi*16 + 4*lk + v, expert
     // wn*64 + ni*16 + lrow
@@ -599,11 +713,15 @@ extern "C" size_t moe_route_workspace_bytes(int T, int H, int N) {
   return (size_t)route_splits(T, H) * (size_t)T * (size_t)N * sizeof(float);
 }
 
-extern "C" moe_status_t moe_route_topk(const void* x_bf16, const void* w_router_bf16,
-                                       const float* bias, int T, int H, int N, int k,
-                                       int n_groups, int topk_groups, float* scores,
-                                       int32_t* topk_idx, float* topk_gate, void* ws,
-                                       size_t ws_bytes, hipStream_t stream) {
+namespace {
+
+// moe_route_topk, and with qx also the 1x128 quantisation of x into x_q / x_d
+// (moe_route_topk_quant_x).
+moe_status_t route_topk_bf16(const void* x_bf16, const void* w_router_bf16, const float* bias,
+                             int T, int H, int N, int k, int n_groups, int topk_groups,
+                             float* scores, int32_t* topk_idx, float* topk_gate, bool qx,
+                             uint8_t* x_q, float* x_d, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
   if (T < 0 || H < 0 || H % 128 != 0 || N < 16 || N > kMaxN || N % 16 != 0 || k < 1 ||
       k > 32 || k > N || !groups_ok(N, k, n_groups, topk_groups))
     return MOE_ERR_SHAPE;
@@ -612,24 +730,53 @@ extern "C" moe_status_t moe_route_topk(const void* x_bf16, const void* w_router_
   // in-kernel byte offsets are 32-bit
   if ((long long)T * H * 2 >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   if (!x_bf16 || !w_router_bf16 || !bias || !topk_idx || !topk_gate) return MOE_ERR_NULL;
+  if (qx && (!x_q || !x_d)) return MOE_ERR_NULL;
   if (!ws || ws_bytes < moe_route_workspace_bytes(T, H, N)) return MOE_ERR_WORKSPACE;
   if (!aligned16(x_bf16) || !aligned16(w_router_bf16) || !aligned16(ws)) return MOE_ERR_ALIGN;
+  if (qx && (!aligned16(x_q) || (reinterpret_cast<uintptr_t>(x_d) & 3))) return MOE_ERR_ALIGN;
   if (moe_status_t st = check_device()) return st;
-  static std::atomic<uint64_t> lds_set{0};
-  if (moe_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(&route_partial_kernel),
-                                          kRLds, lds_set))
-    return st;
+  const void* kern = qx ? reinterpret_cast<const void*>(&route_partial_kernel<true>)
+                        : reinterpret_cast<const void*>(&route_partial_kernel<false>);
+  static std::atomic<uint64_t> lds_set[2] = {0, 0};
+  if (moe_status_t st = allow_dynamic_lds(kern, kRLds, lds_set[qx ? 1 : 0])) return st;
   const int S = route_splits(T, H);
   const int tiles = (T + kRT - 1) / kRT;
   const int grid = (tiles * S + 7) / 8 * 8;
   float* part = static_cast<float*>(ws);
-  hipLaunchKernelGGL(route_partial_kernel, dim3(grid), dim3(kRThreads), kRLds, stream,
-                     static_cast<const uint16_t*>(x_bf16),
-                     static_cast<const uint16_t*>(w_router_bf16), T, H, N, S, part);
+  if (qx)
+    hipLaunchKernelGGL(route_partial_kernel<true>, dim3(grid), dim3(kRThreads), kRLds, stream,
+                       static_cast<const uint16_t*>(x_bf16),
+                       static_cast<const uint16_t*>(w_router_bf16), T, H, N, S, part, x_q, x_d);
+  else
+    hipLaunchKernelGGL(route_partial_kernel<false>, dim3(grid), dim3(kRThreads), kRLds, stream,
+                       static_cast<const uint16_t*>(x_bf16),
+                       static_cast<const uint16_t*>(w_router_bf16), T, H, N, S, part,
+                       (uint8_t*)nullptr, (float*)nullptr);
   if (moe_status_t st = launch_status()) return st;
   launch_finish(part, S, bias, T, N, k, n_groups, topk_groups, scores, topk_idx, topk_gate,
                 stream);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" moe_status_t moe_route_topk(const void* x_bf16, const void* w_router_bf16,
+                                       const float* bias, int T, int H, int N, int k,
+                                       int n_groups, int topk_groups, float* scores,
+                                       int32_t* topk_idx, float* topk_gate, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+  return route_topk_bf16(x_bf16, w_router_bf16, bias, T, H, N, k, n_groups, topk_groups, scores,
+                         topk_idx, topk_gate, false, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+extern "C" moe_status_t moe_route_topk_quant_x(const void* x_bf16, const void* w_router_bf16,
+                                               const float* bias, int T, int H, int N, int k,
+                                               int n_groups, int topk_groups, float* scores,
+                                               int32_t* topk_idx, float* topk_gate,
+                                               uint8_t* x_q, float* x_d, void* ws,
+                                               size_t ws_bytes, hipStream_t stream) {
+  return route_topk_bf16(x_bf16, w_router_bf16, bias, T, H, N, k, n_groups, topk_groups, scores,
+                         topk_idx, topk_gate, true, x_q, x_d, ws, ws_bytes, stream);
 }
 
 extern "C" moe_status_t moe_route_topk_fp8(const uint8_t* x_q, const float* x_d,
@@ -647,7 +794,7 @@ extern "C" moe_status_t moe_route_topk_fp8(const uint8_t* x_q, const float* x_d,
   if ((long long)T * H >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   if (!x_q || !x_d || !w_router_q || !w_router_d || !bias || !topk_idx || !topk_gate)
     return MOE_ERR_NULL;
-  // this path splits H at most as finely as the bf16 one, so the bf16 size bounds it
+  // this path splits H as the bf16 one does, so the bf16 size fits it
   if (!ws || ws_bytes < moe_route_workspace_bytes(T, H, N)) return MOE_ERR_WORKSPACE;
   if (!aligned16(x_q) || !aligned16(w_router_q) || !aligned16(ws) ||
       (reinterpret_cast<uintptr_t>(x_d) & 3) || (reinterpret_cast<uintptr_t>(w_router_d) & 3))
@@ -657,7 +804,7 @@ extern "C" moe_status_t moe_route_topk_fp8(const uint8_t* x_q, const float* x_d,
   if (moe_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(&route_partial_fp8_kernel),
                                           kRLdsF, lds_set))
     return st;
-  const int S = route_splits(T, H / 2);   // one chunk here is 128 codes, not 64
+  const int S = route_splits(T, H);
   const int tiles = (T + kRT - 1) / kRT;
   const int grid = (tiles * S + 7) / 8 * 8;
   float* part = static_cast<float*>(ws);

@@ -94,6 +94,22 @@ moe_status_t moe_route_topk(const void* x_bf16, const void* w_router_bf16, const
                             size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_route_topk plus the 1x128 activation quantisation of x ([TP] section
+ * V, FP8 detail 1 and Figure 6; [DF] part 1, "Per-tile FP8 scaling"), taken
+ * from the same read of x: the scores, top_idx and topk_gate of
+ * moe_route_topk, and x_q uint8 [T,H] (dense, E4M3 codes) with x_d float
+ * [T,H/128], equal bit for bit to fp8_quant_1x128(x_bf16, MOE_BF16, T, H, H,
+ * x_q, x_d).  Same arguments, workspace, limits and errors as moe_route_topk;
+ * x_q (16-byte aligned) and x_d (4-byte aligned) must not be NULL when
+ * T > 0 (MOE_ERR_NULL) and must not overlap x or the workspace.
+ */
+moe_status_t moe_route_topk_quant_x(const void* x_bf16, const void* w_router_bf16,
+                                    const float* bias, int T, int H, int N, int k, int n_groups,
+                                    int topk_groups, float* scores, int32_t* topk_idx,
+                                    float* topk_gate, uint8_t* x_q, float* x_d, void* ws,
+                                    size_t ws_bytes, hipStream_t stream);
+
+/*
  * Opt-in FP8 router: the same scores, selection and gates as moe_route_topk,
  * but the logits come from block-scaled FP8 operands (the product of [TP]
  * section V, FP8 details 1-2, applied to the gating GEMM, which detail 4

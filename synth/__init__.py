@@ -260,11 +260,16 @@ WORKLOADS = {
     "routing": Workload("routing", T=16384, H=7168, N=256, k=8, I=2048, x_std=1.0,
                         wr_dist=NORMAL, wr_param=0.02, bias_half=0.05, w_std=0.006,
                         with_experts=False),
+    # the V3-shaped layers start from a zero bias, as a fresh layer does: a
+    # bias of +-0.05 moves the keys near the top of the sigmoid (where
+    # s (1 - s) is about 0.03) by more than a logit standard deviation and
+    # spreads the rows per expert from 1 to about 700 at T = 8192, where the
+    # prefill batch is meant to load the experts roughly evenly
     "decode": Workload("decode", T=512, H=7168, N=256, k=8, I=2048, x_std=1.0,
-                       wr_dist=NORMAL, wr_param=0.02, bias_half=0.05, w_std=0.006),
+                       wr_dist=NORMAL, wr_param=0.02, bias_half=0.0, w_std=0.006),
     "prefill": Workload("prefill", T=8192, H=7168, N=256, k=8, I=2048, x_std=1.0,
                         wr_dist=UNIFORM, wr_param=0.02 * math.sqrt(3.0),
-                        bias_half=0.05, w_std=0.006),
+                        bias_half=0.0, w_std=0.006),
     "skew": Workload("skew", T=32768, H=7168, N=256, k=8, I=2048, x_std=1.0,
                      wr_dist=NORMAL, wr_param=0.02, bias_half=0.0, w_std=0.006,
                      skew=True, batches=10),

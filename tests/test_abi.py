@@ -29,7 +29,8 @@ def lib():
 
 def test_header_declares_the_layer_calls():
     names = declared_functions()
-    for n in ["moe_route_topk", "moe_route_topk_fp8", "moe_route_workspace_bytes",
+    for n in ["moe_route_topk", "moe_route_topk_quant_x", "moe_route_topk_fp8",
+              "moe_route_workspace_bytes",
               "moe_topk_from_scores", "moe_permute",
               "moe_permute_workspace_bytes", "fp8_quant_1x128", "fp8_quant_128x128",
               "moe_grouped_gemm_fp8", "moe_grouped_gemm_fp8_tiles", "moe_combine", "moe_bias_update", "moe_status_str",
@@ -81,6 +82,15 @@ def test_validation_before_any_launch(lib):
     # missing workspace (checked before any device access)
     assert R(4, 256, 16, 2, x=dummy) == 4
     assert R(4, 256, 256, 8, 8, 4, x=dummy) == 4
+    lib.moe_route_topk_quant_x.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P, P, P,
+                                           ctypes.c_size_t, P]
+    RQ = lambda T, H, N, k, x=None, q=None, ws=None: lib.moe_route_topk_quant_x(  # noqa: E731
+        x, x, x, T, H, N, k, 1, 1, None, x, x, q, q, ws, 0, None)
+    assert RQ(4, 200, 16, 2) == 2                 # H % 128
+    assert RQ(4, 256, 257, 8) == 2
+    assert RQ(0, 256, 16, 2) == 0
+    assert RQ(4, 256, 16, 2, x=dummy) == 1        # no x_q / x_d
+    assert RQ(4, 256, 16, 2, x=dummy, q=dummy) == 4   # missing workspace
     lib.moe_route_topk_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, P, P,
                                        ctypes.c_size_t, P]
     R8 = lambda T, H, N, k, G=1, M=1, x=None, ws=None: lib.moe_route_topk_fp8(  # noqa: E731
@@ -99,7 +109,8 @@ def test_validation_before_any_launch(lib):
     lib.moe_route_workspace_bytes.argtypes = [I, I, I]
     # 8192 tokens of H 7168: 64 token tiles, 4 slices of the 112 chunks
     assert lib.moe_route_workspace_bytes(8192, 7168, 256) == 4 * 8192 * 256 * 4
-    assert lib.moe_route_workspace_bytes(64, 256, 16) == 4 * 64 * 16 * 4
+    # 64 tokens of H 256: one token tile, one slice per 128-wide block of H
+    assert lib.moe_route_workspace_bytes(64, 256, 16) == 2 * 64 * 16 * 4
     assert lib.moe_route_workspace_bytes(0, 256, 16) == 0
     lib.moe_combine.argtypes = [P, P, P, I, I, I, I, P, P, P]
     assert lib.moe_combine(None, None, None, 0, 4, 12, 2, None, None, None) == 2   # H % 8

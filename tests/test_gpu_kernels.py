@@ -292,6 +292,62 @@ def test_route_topk_ragged_small():
         _route_check(x, wr, b, k, s.cpu().numpy(), idx.cpu().numpy(), gate.cpu().numpy())
 
 
+@pytest.mark.parametrize("case", ["tiny", "decode", "prefill-1000", "ragged", "skew-300"])
+def test_route_topk_quant_x(case):
+    """The router that also quantises x: its codes and scales equal the
+    oracle's 1x128 quantisation bit for bit (adversarial rows appended:
+    zero tiles, -0, overflowing 448 / amax, subnormals, an outlier), and its
+    routing equals moe_route_topk's bit for bit (same kernel arithmetic).
+    Shapes span 1-56 blocks of H per row, slices of one to several blocks,
+    token tiles with a ragged last tile, and 16-256 experts."""
+    moe = _moe()
+    rng = np.random.default_rng(11)
+    if case == "ragged":
+        T, H, N, k = 133, 384, 32, 3
+        xb = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+        wrb = synth.f32_to_bf16_bits((rng.standard_normal((N, H)) * 0.05).astype(np.float32))
+        b = rng.uniform(-0.1, 0.1, N).astype(np.float32)
+    else:
+        name, _, rows = case.partition("-")
+        w = synth.WORKLOADS[name]
+        T = int(rows) if rows else w.T
+        xb = synth.generate(w.x_spec(), w.seed, rows=np.arange(T))
+        wrb, b, k, H = w.router_weight(), w.bias(), w.k, w.H
+    xb = np.concatenate([xb, synth.f32_to_bf16_bits(_adversarial_rows(H))])
+    log(f"moe_route_topk_quant_x {case} T={xb.shape[0]} H={H} N={wrb.shape[0]}")
+    x, wr, bd = bf16_to_dev(xb), bf16_to_dev(wrb), to_dev(b)
+    idx, gate, s, q, d = moe.moe_route_topk_quant_x(x, wr, bd, k)
+    idx0, gate0, s0 = moe.moe_route_topk(x, wr, bd, k)
+    torch.cuda.synchronize()
+    wq, wd = quant.quant_1x128(synth.as_f64(xb))
+    assert np.array_equal(q.cpu().numpy(), wq)
+    assert np.array_equal(d.cpu().numpy(), wd)
+    assert torch.equal(idx, idx0) and torch.equal(gate, gate0) and torch.equal(s, s0)
+
+
+def test_route_topk_quant_x_full_prefill():
+    """At the prefill batch's full size (T = 8192, H 7168, 256 experts), in
+    the layer's launch configuration: codes and scales equal
+    fp8_quant_1x128's bit for bit on every token, and the oracle's on a
+    sample of 256 tokens; routing equals moe_route_topk's."""
+    moe = _moe()
+    w = synth.WORKLOADS["prefill"]
+    x = device_tensor(w.x_spec(), w.seed)
+    wr, bd = bf16_to_dev(w.router_weight()), to_dev(w.bias())
+    log(f"moe_route_topk_quant_x prefill T={w.T}")
+    idx, gate, s, q, d = moe.moe_route_topk_quant_x(x, wr, bd, w.k)
+    q1, d1 = moe.fp8_quant_1x128(x)
+    idx0, gate0, s0 = moe.moe_route_topk(x, wr, bd, w.k)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q1) and torch.equal(d, d1)
+    assert torch.equal(idx, idx0) and torch.equal(gate, gate0) and torch.equal(s, s0)
+    rows = np.unique(np.concatenate([[0, w.T - 1], np.random.default_rng(3).integers(0, w.T, 254)]))
+    xb = synth.generate(w.x_spec(), w.seed, rows=rows)
+    wq, wd = quant.quant_1x128(synth.as_f64(xb))
+    assert np.array_equal(q.cpu().numpy()[rows], wq)
+    assert np.array_equal(d.cpu().numpy()[rows], wd)
+
+
 def test_route_topk_full_routing_workload_sampled():
     """The routing workload at its full size (T = 16384, H 7168, 256 experts,
     top-8), in the launch configuration the layer uses; the oracle recomputes
