@@ -56,7 +56,9 @@
 //     offsets (tiles ordered group, column tile (or pair), row tile), so the
 //     call needs no workspace and no host sync; consecutive row tiles of one
 //     (expert, column tile) are mapped to the same XCD so their weight tile is
-//     fetched from HBM once and re-read from that XCD's L2; in a group's last
+//     fetched from HBM once and re-read from that XCD's L2, and the last
+//     group (the shared expert) is cut into 8 column parts spread over the 8
+//     XCDs' runs so that no XCD gets all its full tiles; in a group's last
 //     row tile, 16-row subtiles past the group's end skip their MFMAs (the K
 //     loop is compiled for each count of live subtiles).
 #include <type_traits>
@@ -171,6 +173,96 @@ __device__ __forceinline__ uint32_t row_max16_halving(const uint32_t (&a)[16], i
   return max(s0 ? d[1] : d[0], dpp<0xB1>(s0 ? d[0] : d[1]));               // quad perm: ^1
 }
 
+// ---- the tile list.  Tiles are ordered (group, column tile, row tile): group
+// g owns ceil(rows_g / BMt) row tiles for each of its n_cols column tiles,
+// and consecutive row tiles of one column tile are consecutive in the list.
+// Dispatch sends workgroup b to XCD b % 8, and each XCD takes a contiguous
+// run of the list, so the row tiles that share a weight tile run on one XCD
+// and re-read it from that XCD's L2.  The last group (the shared expert of
+// the layer: T rows, every one a full tile) would put all its tiles on the
+// last XCD, which would then finish last; with at least 8 other groups and 8
+// column tiles it is cut into 8 parts of n_cols / 8 column tiles, part j
+// placed after group (j + 1) (G - 1) / 8 - 1, so every XCD's run holds one
+// part.  Thread t counts the tiles that follow groups t * per .. t * per +
+// per - 1 in the list (per <= 3); a wave-level scan and one pass over the 8
+// wave totals give every thread the exclusive prefix of its groups, and the
+// thread whose range holds this workgroup's tile publishes the group, the
+// tile's index inside the group's part, and the part's first column tile.
+// Returns false when this workgroup has no tile (the same in all its
+// threads).
+template <int BMt>
+__device__ __forceinline__ bool find_tile(const GemmParams& p, int n_cols, int* s_tmp, int tid,
+                                          int lane, int wave, int& g, int& local, int& col0) {
+  const int G = p.G;
+  const bool split = G >= 9 && n_cols >= 8;
+  const int last = G - 1;
+  int last_mt = 0;
+  if (split) {
+    const int r0 = clampi(p.offsets[last], 0, p.total_rows);
+    const int r1 = clampi(p.offsets[last + 1], 0, p.total_rows);
+    last_mt = ((r1 > r0 ? r1 - r0 : 0) + BMt - 1) / BMt;
+  }
+  const int per = (G + kThreads - 1) / kThreads;   // <= 3
+  int cnt[3], own[3], part[3];
+  int run = 0;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int gi = tid * per + i;
+    int c = 0, pj = -1;
+    if (i < per && gi < G && !(split && gi == last)) {
+      const int r0 = clampi(p.offsets[gi], 0, p.total_rows);
+      const int r1 = clampi(p.offsets[gi + 1], 0, p.total_rows);
+      const int rows = r1 > r0 ? r1 - r0 : 0;
+      c = ((rows + BMt - 1) / BMt) * n_cols;
+      if (split) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (((j + 1) * last) / 8 - 1 == gi) pj = j;
+      }
+    }
+    own[i] = c;
+    part[i] = pj;
+    if (pj >= 0) c += last_mt * ((pj + 1) * n_cols / 8 - pj * n_cols / 8);
+    cnt[i] = c;
+    run += c;
+  }
+  int incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) s_tmp[wave] = incl;
+  __syncthreads();
+  int base = incl - run, total = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    const int t = s_tmp[w];
+    if (w < wave) base += t;
+    total += t;
+  }
+  const int per_xcd = (total + 7) / 8;
+  const int slot = blockIdx.x >> 3, xcd = blockIdx.x & 7;
+  const int L = xcd * per_xcd + slot;
+  if (slot >= per_xcd || L >= total) return false;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int gi = tid * per + i;
+    if (i < per && gi < G && L >= base && L < base + cnt[i]) {
+      const bool in_part = L >= base + own[i];
+      s_tmp[8] = in_part ? last : gi;
+      s_tmp[9] = in_part ? L - base - own[i] : L - base;
+      s_tmp[10] = in_part ? part[i] * n_cols / 8 : 0;
+    }
+    base += cnt[i];
+  }
+  __syncthreads();
+  g = __builtin_amdgcn_readfirstlane(s_tmp[8]);
+  local = __builtin_amdgcn_readfirstlane(s_tmp[9]);
+  col0 = __builtin_amdgcn_readfirstlane(s_tmp[10]);
+  return true;
+}
+
 template <int EPI, bool PING_PONG>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -191,70 +283,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   const int per = kPingPong ? 1 : (p.cols_per_wg == 2 ? 2 : 1);
   const int n_cols = (n_tiles + per - 1) / per;
 
-  // ---- tile list: tiles are ordered (group, column tile, row tile), and
-  // group g owns ceil(rows_g / BM) * n_tiles of them.  Thread t counts the
-  // tiles of groups t * per .. t * per + per - 1 (per <= 3); a wave-level scan
-  // and one pass over the 8 wave totals give every thread the exclusive prefix
-  // of its groups, and the thread whose range holds this workgroup's tile
-  // publishes the group and its first tile.
-  int g, local;
-  {
-    const int per = (G + kThreads - 1) / kThreads;   // <= 3
-    int cnt[3];
-    int run = 0;
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int gi = tid * per + i;
-      int c = 0;
-      if (i < per && gi < G) {
-        const int r0 = clampi(p.offsets[gi], 0, p.total_rows);
-        const int r1 = clampi(p.offsets[gi + 1], 0, p.total_rows);
-        const int rows = r1 > r0 ? r1 - r0 : 0;
-        c = ((rows + BM - 1) / BM) * n_cols;
-      }
-      cnt[i] = c;
-      run += c;
-    }
-    int incl = run;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    if (lane == 63) s_tmp[wave] = incl;
-    __syncthreads();
-    int base = incl - run, total = 0;
-#pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) {
-      const int t = s_tmp[w];
-      if (w < wave) base += t;
-      total += t;
-    }
-    // XCD-aware mapping: dispatch sends block b to XCD b % 8; give each XCD
-    // a contiguous run of the tile list.  (total is the same in every thread,
-    // so a workgroup leaves as a whole.)
-    const int per_xcd = (total + 7) / 8;
-    const int slot = blockIdx.x >> 3, xcd = blockIdx.x & 7;
-    const int L = xcd * per_xcd + slot;
-    if (slot >= per_xcd || L >= total) return;
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int gi = tid * per + i;
-      if (i < per && gi < G && L >= base && L < base + cnt[i]) {
-        s_tmp[8] = gi;
-        s_tmp[9] = base;
-      }
-      base += cnt[i];
-    }
-    __syncthreads();
-    g = __builtin_amdgcn_readfirstlane(s_tmp[8]);
-    local = L - s_tmp[9];
-  }
+  int g, local, col0;
+  if (!find_tile<BM>(p, n_cols, s_tmp, tid, lane, wave, g, local, col0)) return;
   const int row0 = clampi(p.offsets[g], 0, p.total_rows);
   const int rows_g = clampi(p.offsets[g + 1], 0, p.total_rows) - row0;
   const int mt = (rows_g + BM - 1) / BM;
-  const int col = local / mt;                           // column tile (or pair)
-  const int m0 = (local - col * mt) * BM;
+  const int col_l = local / mt;
+  const int col = col0 + col_l;                         // column tile (or pair)
+  const int m0 = (local - col_l * mt) * BM;
   const int rows_valid = min(BM, rows_g - m0);
   const int nkb = p.k_dim / BK;
   const int n_here = min(per, n_tiles - per * col);     // column tiles of this workgroup
@@ -910,57 +946,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm256_kernel(GemmParams
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.G;
   const int n_tiles = p.n_out / BN;
-  // ---- tile list: as in the 128-row kernel, with 256-row tiles
-  int g, local;
-  {
-    const int per = (G + kThreads - 1) / kThreads;   // <= 3
-    int cnt[3];
-    int run = 0;
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int gi = tid * per + i;
-      int c = 0;
-      if (i < per && gi < G) {
-        const int r0 = clampi(p.offsets[gi], 0, p.total_rows);
-        const int r1 = clampi(p.offsets[gi + 1], 0, p.total_rows);
-        const int rows = r1 > r0 ? r1 - r0 : 0;
-        c = ((rows + BM256 - 1) / BM256) * n_tiles;
-      }
-      cnt[i] = c;
-      run += c;
-    }
-    int incl = run;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    if (lane == 63) s_tmp[wave] = incl;
-    __syncthreads();
-    int base = incl - run, total = 0;
-#pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) {
-      const int t = s_tmp[w];
-      if (w < wave) base += t;
-      total += t;
-    }
-    const int per_xcd = (total + 7) / 8;
-    const int slot = blockIdx.x >> 3, xcd = blockIdx.x & 7;
-    const int L = xcd * per_xcd + slot;
-    if (slot >= per_xcd || L >= total) return;
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int gi = tid * per + i;
-      if (i < per && gi < G && L >= base && L < base + cnt[i]) {
-        s_tmp[8] = gi;
-        s_tmp[9] = base;
-      }
-      base += cnt[i];
-    }
-    __syncthreads();
-    g = __builtin_amdgcn_readfirstlane(s_tmp[8]);
-    local = L - s_tmp[9];
-  }
+  int g, local, col0;
+  if (!find_tile<BM256>(p, n_tiles, s_tmp, tid, lane, wave, g, local, col0)) return;
   const int row0 = clampi(p.offsets[g], 0, p.total_rows);
   const int rows_g = clampi(p.offsets[g + 1], 0, p.total_rows) - row0;
   // A group's rows are split evenly over its ceil(rows / 256) row tiles (291
@@ -968,8 +955,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm256_kernel(GemmParams
   // side by side on one XCD and share its lines in L2 only while they stay in
   // step; a nearly empty last tile would run ahead and fetch them again.
   const int mt = (rows_g + BM256 - 1) / BM256;
-  const int n_tile = local / mt;
-  const int rt = local - n_tile * mt;
+  const int n_tile_l = local / mt;
+  const int n_tile = col0 + n_tile_l;
+  const int rt = local - n_tile_l * mt;
   const int m0 = (int)((long long)rt * rows_g / mt);
   const int rows_valid = (int)((long long)(rt + 1) * rows_g / mt) - m0;   // <= 256
   const int nkb = p.k_dim / BK;
