@@ -292,7 +292,8 @@ def test_route_topk_ragged_small():
         _route_check(x, wr, b, k, s.cpu().numpy(), idx.cpu().numpy(), gate.cpu().numpy())
 
 
-@pytest.mark.parametrize("case", ["tiny", "decode", "prefill-1000", "ragged", "skew-300"])
+@pytest.mark.parametrize("case", ["tiny", "decode", "prefill-1000", "ragged", "ragged-h128",
+                                  "ragged-h640", "skew-300"])
 def test_route_topk_quant_x(case):
     """The router that also quantises x: its codes and scales equal the
     oracle's 1x128 quantisation bit for bit (adversarial rows appended:
@@ -302,8 +303,9 @@ def test_route_topk_quant_x(case):
     token tiles with a ragged last tile, and 16-256 experts."""
     moe = _moe()
     rng = np.random.default_rng(11)
-    if case == "ragged":
-        T, H, N, k = 133, 384, 32, 3
+    if case.startswith("ragged"):
+        T, H, N, k = {"ragged": (133, 384, 32, 3), "ragged-h128": (33, 128, 16, 16),
+                      "ragged-h640": (129, 640, 80, 6)}[case]
         xb = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
         wrb = synth.f32_to_bf16_bits((rng.standard_normal((N, H)) * 0.05).astype(np.float32))
         b = rng.uniform(-0.1, 0.1, N).astype(np.float32)
