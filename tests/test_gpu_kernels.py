@@ -558,6 +558,13 @@ def _int_codes(rng, shape, lim=4):
     (2048, 7168, [130, 3], False),
     (16384, 256, [3, 130], True),               # the largest K: 128 K blocks
     (1152, 512, [255, 256, 257, 600, 0, 31], True),   # 256-row tiles: evenly split groups
+    # the last group spread over the XCD runs in 8 column parts (at least 8
+    # other groups and 8 column tiles): one column tile per part, parts of
+    # one and two, and 7 column tiles (no spread); empty groups at the part
+    # boundaries
+    (256, 2048, [40, 0, 0, 130, 7, 0, 256, 1, 600], True),
+    (256, 2304, [3, 300, 0, 0, 0, 64, 129, 0, 17, 250, 0, 9, 0, 0, 511, 2, 700], False),
+    (128, 1792, [10, 0, 257, 33, 0, 0, 128, 1, 90, 513], True),
 ])
 def test_gemm_integer_operands_bit_exact(K, n_out, sizes, gather):
     """Integer-valued codes with power-of-two scales: every partial sum is an
