@@ -32,7 +32,6 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kMaxN = 256;
 constexpr int kRT = 128;                        // tokens per workgroup
-constexpr int kRKc = 64;                        // K chunk: 64 bf16 = 128 bytes per row
 constexpr int kRStage = (kRT + kMaxN) * 128;    // 48 KiB: x rows, then Wr rows
 constexpr int kRStages = 3;
 constexpr int kRLds = kRStages * kRStage;       // 144 KiB
@@ -326,14 +325,20 @@ __global__ __launch_bounds__(kRThreads, 1) void route_partial_kernel(
   const int d_row = q_live ? (t0 + qr) * nb * 4 : T * nb * 4;
   const __amdgpu_buffer_rsrc_t rs_q = make_rsrc(xq, QX ? T * H : 0);
   const __amdgpu_buffer_rsrc_t rs_qd = make_rsrc(xd, QX ? T * nb * 4 : 0);
-  uint4 qv0 = make_uint4(0u, 0u, 0u, 0u), qv1 = qv0;      // first chunk's 16 bf16
+  float qu[16];                                             // first chunk's 16 values
+#pragma unroll
+  for (int e = 0; e < 16; ++e) qu[e] = 0.0f;
   float qmax = 0.0f;
   i32x4 q_lo = i32x4{0, 0, 0, 0}, q_hi = q_lo;              // a finished block, not yet stored
+  // scales: thread qp of a row keeps the scale of the slice's blocks 4 m + qp,
+  // and the row's four threads store four blocks' scales as 16 contiguous
+  // bytes (one write, not four)
   float q_d = 1.0f;
+  const int blk0 = c0 >> 1, nblk = nck >> 1;
   // the first K chunk of a block (P = 0): keep its values, start the maximum;
   // the second (P = 1): finish the maximum over the 4 threads of the row,
   // form the scale and encode both chunks
-  auto quant_chunk = [&](auto p_c, const uint4& a, const uint4& b) {
+  auto quant_chunk = [&](auto p_c, const uint4& a, const uint4& b, int blk_done) {
     constexpr int P = decltype(p_c)::value;
     float v[16];
     v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
@@ -344,20 +349,14 @@ __global__ __launch_bounds__(kRThreads, 1) void route_partial_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[e]));
     if constexpr (P == 0) {
-      qv0 = a;
-      qv1 = b;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) qu[e] = v[e];
       qmax = m;
     } else {
       m = group_max<4>(m);
       float mul, dd;
       tile_scale(m, mul, dd);
-      float u[16];
-      u[0] = bf16_lo(qv0.x); u[1] = bf16_hi(qv0.x); u[2] = bf16_lo(qv0.y);
-      u[3] = bf16_hi(qv0.y); u[4] = bf16_lo(qv0.z); u[5] = bf16_hi(qv0.z);
-      u[6] = bf16_lo(qv0.w); u[7] = bf16_hi(qv0.w); u[8] = bf16_lo(qv1.x);
-      u[9] = bf16_hi(qv1.x); u[10] = bf16_lo(qv1.y); u[11] = bf16_hi(qv1.y);
-      u[12] = bf16_lo(qv1.z); u[13] = bf16_hi(qv1.z); u[14] = bf16_lo(qv1.w);
-      u[15] = bf16_hi(qv1.w);
+      const float (&u)[16] = qu;
       i32x4 c_lo, c_hi;
 #pragma unroll
       for (int w4 = 0; w4 < 4; ++w4) {
@@ -372,16 +371,21 @@ __global__ __launch_bounds__(kRThreads, 1) void route_partial_kernel(
         q_lo[w4] = zero ? 0 : c_lo[w4];
         q_hi[w4] = zero ? 0 : c_hi[w4];
       }
-      q_d = dd;
+      q_d = (blk_done & 3) == qp ? dd : q_d;
     }
   };
-  // the codes and scale of the block completed in K chunk i
+  // the codes of the block completed in K chunk i, and after every fourth
+  // block of the slice (and its last) the scales of up to four blocks
   auto quant_store = [&](int i) {
-    const int blk = (c0 + i) >> 1;
+    const int blk = (c0 + i) >> 1, lb = blk - blk0;
     __builtin_amdgcn_raw_buffer_store_b128(q_lo, rs_q, q_row + blk * 128 + 16 * qp, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b128(q_hi, rs_q, q_row + blk * 128 + 64 + 16 * qp, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(q_d), rs_qd,
-                                          qp == 0 ? d_row + blk * 4 : T * nb * 4, 0, 0);
+    if ((lb & 3) == 3 || lb == nblk - 1) {
+      const int first = lb & ~3;                 // slice-local block of this thread: first + qp
+      __builtin_amdgcn_raw_buffer_store_b32(
+          __float_as_int(q_d), rs_qd,
+          first + qp <= lb ? d_row + (blk0 + first + qp) * 4 : T * nb * 4, 0, 0);
+    }
   };
 
   auto kloop = [&](auto ni_c) {
@@ -423,7 +427,7 @@ __global__ __launch_bounds__(kRThreads, 1) void route_partial_kernel(
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
       }
       if (QX) {
-        quant_chunk(p_c, qa, qb);
+        quant_chunk(p_c, qa, qb, ((c0 + i) >> 1) - blk0);
         // the quantiser's vector work between the MFMAs, so that it runs
         // while they do
         if (NI > 0) {
