@@ -248,10 +248,11 @@ __device__ __forceinline__ void wait_and_barrier() {
 // the four threads of a token row each take 16 values of both K chunks of a
 // block (the first chunk's kept in registers until the second lands), the
 // block maximum is a 4-lane reduction, and the codes leave in two 16-byte
-// buffer stores per thread, the scale in one 4-byte store per row; rows past
-// T point past the buffers' ends, where the stores are dropped, so every wave
-// issues the same stores and the copy waits can count them.  The codes and
-// scales are those of fp8_quant_1x128 (the same scale rule and encoder).
+// buffer stores per thread, the scales of four blocks of a row in one
+// 16-byte write by its four threads; rows past T point past the buffers'
+// ends, where the stores are dropped.  The stores go out before the next
+// stage's copies, so the copy waits cover them.  The codes and scales are
+// those of fp8_quant_1x128 (the same scale rule and encoder).
 template <bool QX>
 __global__ __launch_bounds__(kRThreads, 1) void route_partial_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int H, int N, int S,
